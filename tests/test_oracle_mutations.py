@@ -1,0 +1,81 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each test plants one plausible slip into the oracle (by patching it for the
+duration of the test) and checks that a hand-worked block or a layout pin
+now fails.  The mistakes: sub-block index off by one, sc and m swapped,
+d and dmin swapped, the q6 offset dropped, the W4A16 zero's sign flipped,
+the nibble order swapped.
+"""
+import json
+import os
+
+import numpy as np
+
+import oracle
+from oracle import dequantize as dq
+from oracle import layout
+
+from test_oracle_pins import _hand_case, golden
+
+
+def _case(cid):
+    return next(c for c in golden()["cases"] if c["id"] == cid)
+
+
+def _y(case):
+    w, x = _hand_case(case)
+    return oracle.matvec_ref(oracle.dequant(case["fmt"], w), x)[0, 0]
+
+
+def test_pins_pass_unpatched():
+    for c in golden()["cases"]:
+        assert _y(c) == c["y"]
+
+
+def test_subblock_index_off_by_one_is_caught(monkeypatch):
+    orig = dq._expand
+    monkeypatch.setattr(dq, "_expand", lambda a, width: np.roll(orig(a, width), width, axis=-1))
+    bad = [c["id"] for c in golden()["cases"] if _y(c) != c["y"]]
+    assert "q4k_e37" in bad and "q6k_e100" in bad
+
+
+def test_sc_m_swapped_is_caught(monkeypatch):
+    orig = dq.dequant_q4k
+    monkeypatch.setattr(dq, "dequant_q4k", lambda q, sc, m, d, dmin: orig(q, m, sc, d, dmin))
+    assert _y(_case("q4k_ones")) != 3872.0
+
+
+def test_d_dmin_swapped_is_caught(monkeypatch):
+    orig = dq.dequant_q4k
+    monkeypatch.setattr(dq, "dequant_q4k", lambda q, sc, m, d, dmin: orig(q, sc, m, dmin, d))
+    assert _y(_case("q4k_ones")) != 3872.0
+
+
+def test_q6_offset_dropped_is_caught(monkeypatch):
+    orig = dq.dequant_q6k
+    # q - 32 -> q - 0: emulate by adding 32 to q before the oracle subtracts it
+    monkeypatch.setattr(dq, "dequant_q6k", lambda q, s, d: orig(np.asarray(q) + 32, s, d))
+    assert _y(_case("q6k_e100")) != -1.0
+
+
+def test_zero_sign_flipped_is_caught(monkeypatch):
+    orig = dq.f16_to_f32
+    # flip the sign bit of the zero only: patch dequant_w4a16_g64's zero argument
+    o = dq.dequant_w4a16_g64
+    monkeypatch.setattr(dq, "dequant_w4a16_g64",
+                        lambda q, s, z: o(q, s, (np.asarray(z, np.uint16) ^ 0x8000).astype(np.uint16)))
+    assert _y(_case("w4a16_ones")) != -8.0
+    del orig
+
+
+def test_nibble_order_swapped_is_caught(monkeypatch):
+    def swapped(q):
+        q = np.asarray(q, dtype=np.uint8) & 0xF
+        return (q[:, 1::2] | (q[:, 0::2] << 4)).astype(np.uint8)
+    monkeypatch.setattr(layout, "_nibbles", swapped)
+    k = np.arange(64)
+    w = {"q": (k % 16).astype(np.uint8)[None], "scale": np.array([[0x3400]], np.uint16),
+         "zero": np.array([[0x4800]], np.uint16)}
+    buf = oracle.pack_ref("w4a16_g64", w)
+    want = {c["id"]: c for c in golden()["packed"]}["w4a16_qs_bytes"]["bytes"]
+    assert buf[0] != int(want["0"], 16)
