@@ -1,0 +1,179 @@
+"""Python binding of libqmv: fused dequantize-and-multiply of block-quantized
+weights on MI355X (gfx950).
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels of libqmv.so; PyTorch supplies device memory and the current stream.
+Importing this package fails loudly when the library has not been built
+(`python -m gemm_dequant_matvec_amd.build`); there is no CPU fallback.
+
+    import gemm_dequant_matvec_amd as qmv
+    W = qmv.pack("q4k", {"q": q, "sc": sc, "m": m, "d": d, "dmin": dmin})
+    y = qmv.matvec("q4k", W, x, N, K)          # x [b][K] f32 -> y [b][N] f32
+    Y = qmv.gemm("w4a16_g64", W, X, N, K)      # X [M][K] bf16 -> Y [M][N] bf16
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqmv.so")
+
+FORMATS = {"q8_0": 1, "w4a16_g64": 2, "q4k": 3, "q6k": 4}
+BLOCK = {"q8_0": 32, "w4a16_g64": 64, "q4k": 256, "q6k": 256}
+AUX_FIELDS = {
+    "q8_0": ("scale",),
+    "w4a16_g64": ("scale", "zero"),
+    "q4k": ("sc", "m", "d", "dmin"),
+    "q6k": ("s", "d"),
+}
+_DTYPES = {torch.float32: 1, torch.float16: 2, torch.bfloat16: 3}
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"libqmv.so not found at {LIB_PATH}: build it with "
+        "`python -m gemm_dequant_matvec_amd.build` (hipcc, gfx950)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+class QmvLogical(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("aux", ctypes.c_void_p * 4)]
+
+
+_i64, _vp, _int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+_lib.qmv_abi_version.argtypes = [ctypes.POINTER(ctypes.c_int)]
+_lib.qmv_abi_version.restype = _int
+_lib.qmv_status_string.argtypes = [_int]
+_lib.qmv_status_string.restype = ctypes.c_char_p
+_lib.qmv_last_error.argtypes = []
+_lib.qmv_last_error.restype = ctypes.c_char_p
+_lib.qmv_packed_bytes.argtypes = [_int, _i64, _i64, _i64, ctypes.POINTER(ctypes.c_size_t)]
+_lib.qmv_packed_bytes.restype = _int
+_lib.qmv_pack.argtypes = [_int, _i64, _i64, _i64, ctypes.POINTER(QmvLogical), _vp, _vp]
+_lib.qmv_pack.restype = _int
+_lib.qmv_matvec.argtypes = [_int, _i64, _i64, _i64, _vp, _vp, _int, _vp, _int, _vp]
+_lib.qmv_matvec.restype = _int
+_lib.qmv_gemm.argtypes = [_int, _i64, _i64, _i64, _vp, _vp, _int, _vp, _int, _vp]
+_lib.qmv_gemm.restype = _int
+_lib.qmv_dequant.argtypes = [_int, _i64, _i64, _vp, _vp, _vp]
+_lib.qmv_dequant.restype = _int
+
+EXPORTS = ("qmv_abi_version", "qmv_status_string", "qmv_last_error", "qmv_packed_bytes",
+           "qmv_pack", "qmv_matvec", "qmv_gemm", "qmv_dequant")
+
+
+class QmvError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        super().__init__(f"{_lib.qmv_status_string(status).decode()} ({status}): {message}")
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise QmvError(status, _lib.qmv_last_error().decode())
+
+
+def _fmt(fmt) -> int:
+    if isinstance(fmt, str):
+        if fmt not in FORMATS:
+            raise ValueError(f"unknown format {fmt!r}; one of {sorted(FORMATS)}")
+        return FORMATS[fmt]
+    return int(fmt)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors passed to libqmv must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libqmv must be contiguous")
+    return t.data_ptr()
+
+
+def abi_version() -> tuple[int, int]:
+    lv = ctypes.c_int(0)
+    v = _lib.qmv_abi_version(ctypes.byref(lv))
+    return v, lv.value
+
+
+def packed_bytes(fmt, N: int, K: int, batch: int = 1) -> int:
+    out = ctypes.c_size_t(0)
+    _check(_lib.qmv_packed_bytes(_fmt(fmt), N, K, batch, ctypes.byref(out)))
+    return out.value
+
+
+def pack(fmt, logical: dict, N: int | None = None, K: int | None = None, batch: int = 1,
+         out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Pack logical device arrays (dict of tensors named as in AUX_FIELDS plus "q")."""
+    name = fmt if isinstance(fmt, str) else {v: k for k, v in FORMATS.items()}[fmt]
+    q = logical["q"]
+    if N is None or K is None:
+        N, K = q.shape[-2], q.shape[-1]
+    nbytes = packed_bytes(name, N, K, batch)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    src = QmvLogical()
+    src.q = _ptr(q)
+    for i, field in enumerate(AUX_FIELDS[name]):
+        src.aux[i] = _ptr(logical[field])
+    _check(_lib.qmv_pack(_fmt(name), N, K, batch, ctypes.byref(src), _ptr(out), _stream(stream)))
+    return out
+
+
+def matvec(fmt, W: torch.Tensor, x: torch.Tensor, N: int, K: int, y: torch.Tensor | None = None,
+           stream=None) -> torch.Tensor:
+    """y [b][N] f32 = W x for x [b][K] (f32, or f16 for w4a16_g64)."""
+    x2 = x if x.dim() == 2 else x.reshape(1, -1)
+    b = x2.shape[0]
+    if x2.shape[1] != K:
+        raise ValueError(f"x has {x2.shape[1]} columns, expected K={K}")
+    if y is None:
+        y = torch.empty((b, N), dtype=torch.float32, device=x.device)
+    if x2.dtype not in _DTYPES or y.dtype not in _DTYPES:
+        raise ValueError("x / y dtype must be float32, float16 or bfloat16")
+    _check(_lib.qmv_matvec(_fmt(fmt), N, K, b, _ptr(W), _ptr(x2), _DTYPES[x2.dtype], _ptr(y),
+                           _DTYPES[y.dtype], _stream(stream)))
+    return y
+
+
+def gemm(fmt, W: torch.Tensor, X: torch.Tensor, N: int, K: int, Y: torch.Tensor | None = None,
+         stream=None) -> torch.Tensor:
+    """Y [M][N] bf16 = X W^T for X [M][K] bf16, on the matrix cores."""
+    M = X.shape[0]
+    if X.shape[1] != K:
+        raise ValueError(f"X has {X.shape[1]} columns, expected K={K}")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    if X.dtype not in _DTYPES or Y.dtype not in _DTYPES:
+        raise ValueError("X / Y dtype must be float32, float16 or bfloat16")
+    _check(_lib.qmv_gemm(_fmt(fmt), N, K, M, _ptr(W), _ptr(X), _DTYPES[X.dtype], _ptr(Y),
+                         _DTYPES[Y.dtype], _stream(stream)))
+    return Y
+
+
+def dequant(fmt, W: torch.Tensor, N: int, K: int, out: torch.Tensor | None = None,
+            stream=None) -> torch.Tensor:
+    """Dense f32 [N][K] copy of a packed matrix (bit-exact; inspection/testing)."""
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.float32, device=W.device)
+    _check(_lib.qmv_dequant(_fmt(fmt), N, K, _ptr(W), _ptr(out), _stream(stream)))
+    return out
+
+
+def raw_call(name: str, *args) -> int:
+    """Call a C entry point with raw arguments (tests of the ABI's error paths)."""
+    return getattr(_lib, name)(*args)
+
+
+def last_error() -> str:
+    return _lib.qmv_last_error().decode()

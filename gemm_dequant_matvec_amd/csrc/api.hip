@@ -1,0 +1,226 @@
+// C ABI of libqmv: argument validation, error reporting and dispatch.
+//
+// Unsupported or malformed requests are rejected on the host, before any
+// launch, with a message naming the argument or the missing capability
+// (aot-llm README: unsupported tensor types are rejected with a message
+// naming the tensor; pytensor-ml issue 53, PR 18 acceptance rules: fail with
+// the missing capability named, not at token 1).
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "qmv_internal.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return QMV_OK;
+}
+
+const char* fmt_name(int fmt) {
+  switch (fmt) {
+    case QMV_Q8_0: return "Q8_0";
+    case QMV_W4A16_G64: return "W4A16_G64";
+    case QMV_Q4K: return "Q4K";
+    case QMV_Q6K: return "Q6K";
+    default: return "?";
+  }
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Per-device architecture check, cached after the first query.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+    return fail(QMV_ERR_DEVICE, "hipGetDevice failed (no HIP device?)");
+  if (dev < kMaxDevices) {
+    const int st = g_dev_state[dev].load(std::memory_order_relaxed);
+    if (st == 1) return QMV_OK;
+    if (st == -1) return fail(QMV_ERR_DEVICE, "device %d is not gfx950", dev);
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+    return fail(QMV_ERR_DEVICE, "hipGetDeviceProperties(%d) failed", dev);
+  const bool is950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_dev_state[dev].store(is950 ? 1 : -1, std::memory_order_relaxed);
+  if (!is950) return fail(QMV_ERR_DEVICE, "device %d is %s, the library is built for gfx950", dev,
+                          prop.gcnArchName);
+  return QMV_OK;
+}
+
+int check_fmt(int fmt) {
+  if (qmv::block_of(fmt) == 0) return fail(QMV_ERR_FORMAT, "unknown format %d", fmt);
+  return QMV_OK;
+}
+
+// N, K, batch sanity and size limits shared by all entry points.
+int check_shape(int fmt, int64_t N, int64_t K, int64_t batch, const char* batch_name) {
+  const int blk = qmv::block_of(fmt);
+  if (N < 1) return fail(QMV_ERR_SHAPE, "N=%lld must be >= 1", (long long)N);
+  if (K < 1) return fail(QMV_ERR_SHAPE, "K=%lld must be >= 1", (long long)K);
+  if (K % blk) return fail(QMV_ERR_SHAPE, "K=%lld is not a multiple of the %s block (%d)",
+                           (long long)K, fmt_name(fmt), blk);
+  if (batch < 1) return fail(QMV_ERR_SHAPE, "%s=%lld must be >= 1", batch_name, (long long)batch);
+  // kernels index rows and K with 32-bit ints and planes with 64-bit offsets
+  const int64_t lim = int64_t(1) << 31;
+  if (N >= lim || K >= lim) return fail(QMV_ERR_OVERFLOW, "N or K too large for 32-bit indexing");
+  if (N > (int64_t(1) << 62) / K) return fail(QMV_ERR_OVERFLOW, "N*K overflows");
+  return QMV_OK;
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(QMV_ERR_LAUNCH, "%s launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int qmv_abi_version(int* layout_version) {
+  if (layout_version) *layout_version = QMV_LAYOUT_VERSION;
+  return QMV_ABI_VERSION;
+}
+
+const char* qmv_status_string(int status) {
+  switch (status) {
+    case QMV_OK: return "ok";
+    case QMV_ERR_NULL: return "null pointer";
+    case QMV_ERR_FORMAT: return "unknown format";
+    case QMV_ERR_UNSUPPORTED: return "unsupported";
+    case QMV_ERR_SHAPE: return "bad shape";
+    case QMV_ERR_ALIGN: return "misaligned pointer";
+    case QMV_ERR_DTYPE: return "bad dtype";
+    case QMV_ERR_OVERFLOW: return "size overflow";
+    case QMV_ERR_DEVICE: return "device error";
+    case QMV_ERR_LAUNCH: return "launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* qmv_last_error(void) { return g_last_error; }
+
+int qmv_packed_bytes(int fmt, int64_t N, int64_t K, int64_t batch, size_t* out_bytes) {
+  int st;
+  if ((st = check_fmt(fmt))) return st;
+  if ((st = check_shape(fmt, N, K, batch, "batch"))) return st;
+  if (!out_bytes) return fail(QMV_ERR_NULL, "out_bytes is NULL");
+  const qmv::Planes p = qmv::planes_of(fmt, N, K);
+  if (batch > INT64_MAX / p.total) return fail(QMV_ERR_OVERFLOW, "batch * packed bytes overflows");
+  *out_bytes = static_cast<size_t>(batch * p.total);
+  return ok();
+}
+
+int qmv_pack(int fmt, int64_t N, int64_t K, int64_t batch, const qmv_logical* src, void* dst,
+             void* stream) {
+  int st;
+  if ((st = check_fmt(fmt))) return st;
+  if ((st = check_shape(fmt, N, K, batch, "batch"))) return st;
+  if (batch > 65535) return fail(QMV_ERR_OVERFLOW, "batch=%lld exceeds 65535", (long long)batch);
+  if (!src) return fail(QMV_ERR_NULL, "src is NULL");
+  if (!dst) return fail(QMV_ERR_NULL, "dst is NULL");
+  if (!src->q) return fail(QMV_ERR_NULL, "src->q is NULL");
+  const int naux = fmt == QMV_Q8_0 ? 1 : fmt == QMV_W4A16_G64 ? 2 : fmt == QMV_Q4K ? 4 : 2;
+  for (int i = 0; i < naux; ++i)
+    if (!src->aux[i]) return fail(QMV_ERR_NULL, "src->aux[%d] is NULL (%s needs %d)", i, fmt_name(fmt), naux);
+  if (!aligned(dst, 16)) return fail(QMV_ERR_ALIGN, "dst is not 16-byte aligned");
+  for (int i = 0; i < naux; ++i)
+    if (!aligned(src->aux[i], 2)) return fail(QMV_ERR_ALIGN, "src->aux[%d] is not 2-byte aligned", i);
+  const qmv::Planes p = qmv::planes_of(fmt, N, K);
+  if (batch > INT64_MAX / p.total) return fail(QMV_ERR_OVERFLOW, "batch * packed bytes overflows");
+  if ((N * K + 255) / 256 >= (int64_t(1) << 31))
+    return fail(QMV_ERR_OVERFLOW, "matrix too large for one pack launch");
+  if ((st = check_device())) return st;
+  return launched(qmv::launch_pack(fmt, N, K, batch, *src, static_cast<uint8_t*>(dst), as_stream(stream)),
+                  "pack");
+}
+
+int qmv_matvec(int fmt, int64_t N, int64_t K, int64_t batch, const void* W, const void* x,
+               int x_dtype, void* y, int y_dtype, void* stream) {
+  int st;
+  if ((st = check_fmt(fmt))) return st;
+  if ((st = check_shape(fmt, N, K, batch, "batch"))) return st;
+  if (!W) return fail(QMV_ERR_NULL, "W is NULL");
+  if (!x) return fail(QMV_ERR_NULL, "x is NULL");
+  if (!y) return fail(QMV_ERR_NULL, "y is NULL");
+  if (x_dtype != QMV_F32 && x_dtype != QMV_F16 && x_dtype != QMV_BF16)
+    return fail(QMV_ERR_DTYPE, "x_dtype=%d is not a qmv_dtype", x_dtype);
+  if (y_dtype != QMV_F32 && y_dtype != QMV_F16 && y_dtype != QMV_BF16)
+    return fail(QMV_ERR_DTYPE, "y_dtype=%d is not a qmv_dtype", y_dtype);
+  if (x_dtype == QMV_BF16 || (x_dtype == QMV_F16 && fmt != QMV_W4A16_G64))
+    return fail(QMV_ERR_UNSUPPORTED, "%s matvec takes x as f32%s", fmt_name(fmt),
+                fmt == QMV_W4A16_G64 ? " or f16" : "");
+  if (y_dtype != QMV_F32) return fail(QMV_ERR_UNSUPPORTED, "matvec writes y as f32 only");
+  if (!aligned(W, 16)) return fail(QMV_ERR_ALIGN, "W is not 16-byte aligned");
+  if (!aligned(x, 16)) return fail(QMV_ERR_ALIGN, "x is not 16-byte aligned");
+  if (!aligned(y, 4)) return fail(QMV_ERR_ALIGN, "y is not 4-byte aligned");
+  const int64_t lim = int64_t(1) << 31;
+  if (N * 16 >= lim) return fail(QMV_ERR_OVERFLOW, "N=%lld too large for the row grid", (long long)N);
+  if ((st = check_device())) return st;
+  return launched(qmv::launch_matvec(fmt, N, K, batch, static_cast<const uint8_t*>(W), x, x_dtype,
+                                     static_cast<float*>(y), as_stream(stream)),
+                  "matvec");
+}
+
+int qmv_gemm(int fmt, int64_t N, int64_t K, int64_t M, const void* W, const void* X, int x_dtype,
+             void* Y, int y_dtype, void* stream) {
+  int st;
+  if ((st = check_fmt(fmt))) return st;
+  if ((st = check_shape(fmt, N, K, M, "M"))) return st;
+  if (!W) return fail(QMV_ERR_NULL, "W is NULL");
+  if (!X) return fail(QMV_ERR_NULL, "X is NULL");
+  if (!Y) return fail(QMV_ERR_NULL, "Y is NULL");
+  if (x_dtype != QMV_F32 && x_dtype != QMV_F16 && x_dtype != QMV_BF16)
+    return fail(QMV_ERR_DTYPE, "x_dtype=%d is not a qmv_dtype", x_dtype);
+  if (y_dtype != QMV_F32 && y_dtype != QMV_F16 && y_dtype != QMV_BF16)
+    return fail(QMV_ERR_DTYPE, "y_dtype=%d is not a qmv_dtype", y_dtype);
+  if (fmt != QMV_W4A16_G64)
+    return fail(QMV_ERR_UNSUPPORTED, "gemm supports W4A16_G64 only (got %s)", fmt_name(fmt));
+  if (x_dtype != QMV_BF16 || y_dtype != QMV_BF16)
+    return fail(QMV_ERR_UNSUPPORTED, "gemm takes X and writes Y as bf16");
+  if (!aligned(W, 16)) return fail(QMV_ERR_ALIGN, "W is not 16-byte aligned");
+  if (!aligned(X, 16)) return fail(QMV_ERR_ALIGN, "X is not 16-byte aligned");
+  if (!aligned(Y, 4)) return fail(QMV_ERR_ALIGN, "Y is not 4-byte aligned");
+  if (M >= (int64_t(1) << 31)) return fail(QMV_ERR_OVERFLOW, "M too large");
+  if ((st = check_device())) return st;
+  return launched(qmv::launch_gemm(fmt, N, K, M, static_cast<const uint8_t*>(W),
+                                   static_cast<const uint16_t*>(X), static_cast<uint16_t*>(Y),
+                                   as_stream(stream)),
+                  "gemm");
+}
+
+int qmv_dequant(int fmt, int64_t N, int64_t K, const void* W, float* out, void* stream) {
+  int st;
+  if ((st = check_fmt(fmt))) return st;
+  if ((st = check_shape(fmt, N, K, 1, "batch"))) return st;
+  if (!W) return fail(QMV_ERR_NULL, "W is NULL");
+  if (!out) return fail(QMV_ERR_NULL, "out is NULL");
+  if (!aligned(W, 16)) return fail(QMV_ERR_ALIGN, "W is not 16-byte aligned");
+  if (!aligned(out, 16)) return fail(QMV_ERR_ALIGN, "out is not 16-byte aligned");
+  if ((N * (K / 32) + 255) / 256 >= (int64_t(1) << 31))
+    return fail(QMV_ERR_OVERFLOW, "matrix too large for one dequant launch");
+  if ((st = check_device())) return st;
+  return launched(qmv::launch_dequant(fmt, N, K, static_cast<const uint8_t*>(W), out, as_stream(stream)),
+                  "dequant");
+}
+
+}  // extern "C"

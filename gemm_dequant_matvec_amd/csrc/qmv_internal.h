@@ -1,0 +1,87 @@
+// Internal declarations of libqmv: packed-plane geometry, device helpers and
+// the kernel launchers each translation unit provides to the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/qmv.h"
+
+namespace qmv {
+
+// ----------------------------------------------------------------- geometry
+
+// Weights per scale block, and per K-divisibility unit, of each format.
+constexpr int kBlockQ8_0 = 32;
+constexpr int kGroupW4 = 64;
+constexpr int kSuper = 256;
+
+inline int block_of(int fmt) {
+  switch (fmt) {
+    case QMV_Q8_0: return kBlockQ8_0;
+    case QMV_W4A16_G64: return kGroupW4;
+    case QMV_Q4K: return kSuper;
+    case QMV_Q6K: return kSuper;
+    default: return 0;
+  }
+}
+
+__host__ __device__ inline int64_t round256(int64_t v) { return (v + 255) & ~int64_t(255); }
+
+// Byte offsets of the planes of one packed matrix (layout version 1).
+struct Planes {
+  int64_t off[4];
+  int64_t bytes[4];
+  int count;
+  int64_t total;  // bytes of one packed matrix (multiple of 256)
+};
+
+inline Planes planes_of(int fmt, int64_t N, int64_t K) {
+  Planes p{};
+  int64_t b[4] = {0, 0, 0, 0};
+  int n = 0;
+  switch (fmt) {
+    case QMV_Q8_0: b[0] = N * K; b[1] = N * (K / 32) * 2; n = 2; break;
+    case QMV_W4A16_G64: b[0] = N * K / 2; b[1] = N * (K / 64) * 4; n = 2; break;
+    case QMV_Q4K: b[0] = N * K / 2; b[1] = N * (K / 256) * 16; n = 2; break;
+    case QMV_Q6K:
+      b[0] = N * K / 2; b[1] = N * (K / 16) * 4; b[2] = N * (K / 16); b[3] = N * (K / 256) * 2;
+      n = 4; break;
+    default: break;
+  }
+  int64_t off = 0;
+  for (int i = 0; i < n; ++i) {
+    p.off[i] = off;
+    p.bytes[i] = b[i];
+    off += round256(b[i]);
+  }
+  p.count = n;
+  p.total = off;
+  return p;
+}
+
+// ----------------------------------------------------------- device helpers
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t bits) {
+  // hardware conversion; fp16 denormals are honoured (default float mode)
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits) {
+  return __builtin_bit_cast(float, bits << 16);
+}
+
+// ----------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error; arguments are already validated.
+
+hipError_t launch_pack(int fmt, int64_t N, int64_t K, int64_t batch, const qmv_logical& src,
+                       uint8_t* dst, hipStream_t s);
+hipError_t launch_dequant(int fmt, int64_t N, int64_t K, const uint8_t* W, float* out,
+                          hipStream_t s);
+hipError_t launch_matvec(int fmt, int64_t N, int64_t K, int64_t batch, const uint8_t* W,
+                         const void* x, int x_dtype, float* y, hipStream_t s);
+hipError_t launch_gemm(int fmt, int64_t N, int64_t K, int64_t M, const uint8_t* W,
+                       const uint16_t* X, uint16_t* Y, hipStream_t s);
+
+}  // namespace qmv

@@ -1,0 +1,189 @@
+/*
+ * qmv.h -- fused dequantize-and-multiply of block-quantized weights on
+ * AMD Instinct MI355X (gfx950).  C ABI of libqmv.so.
+ *
+ * What the library computes
+ *   y = W x     (decode matvec, a batch of 1..N activation vectors)
+ *   Y = X W^T   (prefill GEMM on the matrix cores, small M)
+ * directly from packed blocks of small integers with per-block fp16 scales
+ * (and mins or zeros), without ever forming the dense W.  The formats are
+ * those the pages name: the "packed group-64 W4A16 linear kernels" (llmopt
+ * README, "Current compiler and runtime"), Q8_0 and the K-quant Q4_K / Q6_K
+ * matvec kernels (aot-llm README, feature list "Static code generation" and
+ * "SIMD kernels"), and the Q4_K linear of the llmopt parity receipt
+ * ("GGUF-FX parity probe").  The pages give no bit layout or formula; the
+ * definitions below are this library's own, and normative.
+ *
+ * Dequantization (IEEE f32, round to nearest even, in this order, no fusion):
+ *   QMV_Q8_0       32-weight blocks:  w = f32(scale) * f32(q),  q int8
+ *   QMV_W4A16_G64  64-weight groups:  w = f32(scale) * (f32(q) - f32(zero)),  q in 0..15
+ *   QMV_Q4K        256-weight super-blocks of 8 sub-blocks of 32:
+ *                  w = (f32(d) * f32(sc_j)) * f32(q) - f32(dmin) * f32(m_j)
+ *                  q in 0..15, sc_j and m_j in 0..63
+ *   QMV_Q6K        256-weight super-blocks of 16 sub-blocks of 16:
+ *                  w = (f32(d) * f32(s_j)) * (f32(q) - 32),  q in 0..63, s_j int8
+ * The scale of weight k is that of block floor(k / block size).  fp16
+ * subnormals are honoured.  qmv_dequant reproduces these values bit for bit.
+ * qmv_matvec / qmv_gemm may reassociate sums (tolerances below).
+ *
+ * Logical (unpacked) arrays -- the interchange form taken by qmv_pack,
+ * row-major, `batch` matrices stacked back to back:
+ *   Q8_0       q int8 [N][K];  aux[0] scale f16 [N][K/32]
+ *   W4A16_G64  q uint8 [N][K];  aux[0] scale f16 [N][K/64];  aux[1] zero f16 [N][K/64]
+ *   Q4K        q uint8 [N][K];  aux[0] sc uint8 [N][K/32];  aux[1] m uint8 [N][K/32];
+ *              aux[2] d f16 [N][K/256];  aux[3] dmin f16 [N][K/256]
+ *   Q6K        q uint8 [N][K];  aux[0] s int8 [N][K/16];  aux[1] d f16 [N][K/256]
+ * Fields wider than their bit width are masked to it by qmv_pack
+ * (4 bits for 4-bit q, 6 bits for Q6K q and for sc / m).
+ *
+ * Packed layout, version 1 (QMV_LAYOUT_VERSION).  One matrix is a sequence
+ * of planes; every plane starts at a multiple of 256 bytes (plane sizes are
+ * rounded up to 256).  Matrix i of a stack starts at i * qmv_packed_bytes(..,1).
+ * Multi-byte fields are little-endian.
+ *   Q8_0       qs    N*K bytes:      byte n*K + k = q[n][k]
+ *              scale N*(K/32) f16:   element n*(K/32) + b = scale[n][b]
+ *   W4A16_G64  qs    N*K/2 bytes:    byte n*K/2 + j = q[n][2j] | q[n][2j+1] << 4
+ *              sz    N*(K/64) u32:   word n*(K/64) + g = scale[n][g] | zero[n][g] << 16
+ *   Q4K        qs    as W4A16_G64
+ *              meta  N*(K/256) 16-byte records; record (n, t): bytes 0-1 d, bytes 2-3
+ *                    dmin, bytes 4..15 a 96-bit little-endian integer holding
+ *                    sc[n][8t+j] at bits 6j..6j+5 and m[n][8t+j] at bits 48+6j..48+6j+5
+ *   Q6K        ql    N*K/2 bytes: low 4 bits of q, nibble order as W4A16_G64
+ *              qh    N*(K/16) u32: word (n, t) covers k = 16t..16t+15; its bits
+ *                    8c+2f .. 8c+2f+1 (c, f in 0..3) hold bits 4-5 of
+ *                    q[n][16t + 8*(f>>1) + 2c + (f&1)]
+ *              s     N*(K/16) int8
+ *              d     N*(K/256) f16
+ * Bytes per weight including scales: Q8_0 8.5 bits, W4A16_G64 4.5, Q4K 4.5, Q6K 6.5625.
+ *
+ * Accuracy of the products.  For every output,
+ *   |y - y_exact| <= tau * ||W_row||_2 * ||x||_2
+ * with tau = 1e-3 for qmv_matvec (f32 accumulation) and tau = 2e-2 for
+ * qmv_gemm (bf16 matrix-core inputs, bf16 output).  With a one-hot x the
+ * matvec returns the dequantized column bit for bit.
+ *
+ * Ownership and threading.  The caller allocates and owns every buffer; all
+ * pointers passed to compute calls are device pointers.  The compute calls
+ * never allocate, free, synchronize or copy between host and device; they
+ * enqueue kernels on `stream` (a hipStream_t; NULL = the null stream) and
+ * return at once, so they may be captured in a hipGraph.  The library keeps
+ * no state but a per-device architecture check; calls are thread-safe.
+ *
+ * Errors.  Every call returns QMV_OK (0) or a negative qmv_status.  All
+ * argument errors are found on the host before anything is enqueued; the
+ * thread-local qmv_last_error() then names the argument.  QMV_ERR_LAUNCH
+ * reports a failed launch; faults during execution surface at the caller's
+ * next synchronization, as usual for HIP.
+ */
+#ifndef QMV_H_
+#define QMV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QMV_ABI_VERSION 1
+#define QMV_LAYOUT_VERSION 1
+
+enum qmv_format {
+  QMV_Q8_0 = 1,
+  QMV_W4A16_G64 = 2,
+  QMV_Q4K = 3,
+  QMV_Q6K = 4
+};
+
+enum qmv_dtype {
+  QMV_F32 = 1,
+  QMV_F16 = 2,
+  QMV_BF16 = 3
+};
+
+enum qmv_status {
+  QMV_OK = 0,
+  QMV_ERR_NULL = -1,        /* a required pointer is NULL */
+  QMV_ERR_FORMAT = -2,      /* unknown format value */
+  QMV_ERR_UNSUPPORTED = -3, /* valid but not implemented (format / dtype / op) */
+  QMV_ERR_SHAPE = -4,       /* N < 1, K < 1, K not a multiple of the block, batch < 1 */
+  QMV_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned */
+  QMV_ERR_DTYPE = -6,       /* unknown dtype value */
+  QMV_ERR_OVERFLOW = -7,    /* a size does not fit in size_t / int32 indexing */
+  QMV_ERR_DEVICE = -8,      /* current device is not gfx950 or HIP query failed */
+  QMV_ERR_LAUNCH = -9       /* hipGetLastError after the launch */
+};
+
+/* Per-format logical arrays for qmv_pack (device pointers); see above. */
+typedef struct qmv_logical {
+  const void* q;
+  const void* aux[4];
+} qmv_logical;
+
+/* ABI version (QMV_ABI_VERSION); *layout_version receives QMV_LAYOUT_VERSION if non-NULL. */
+int qmv_abi_version(int* layout_version);
+
+/* Static text for a status code. */
+const char* qmv_status_string(int status);
+
+/* Thread-local message of the last failing call on this thread ("" if none). */
+const char* qmv_last_error(void);
+
+/*
+ * Bytes of `batch` stacked packed matrices of shape N x K.  Host only.
+ * Errors: FORMAT, SHAPE, NULL (out_bytes), OVERFLOW.
+ */
+int qmv_packed_bytes(int fmt, int64_t N, int64_t K, int64_t batch, size_t* out_bytes);
+
+/*
+ * Pack `batch` stacked logical matrices (device arrays as listed above) into
+ * dst (device, qmv_packed_bytes bytes, 256-byte aligned recommended, 16
+ * required).  Integer bit placement only (pytensor-ml issue 53, PR 17: a
+ * one-time repack, done once per matrix outside the token loop).
+ * Errors: FORMAT, SHAPE, NULL, ALIGN, OVERFLOW, DEVICE, LAUNCH.
+ */
+int qmv_pack(int fmt, int64_t N, int64_t K, int64_t batch, const qmv_logical* src,
+             void* dst, void* stream);
+
+/*
+ * y[b][n] = sum_k W[n][k] * x[b][k] for b < batch, n < N.
+ *   W  packed matrix (device), layout above
+ *   x  [batch][K] of x_dtype (QMV_F32 or QMV_F16), device, 16-byte aligned
+ *   y  [batch][N] of y_dtype (QMV_F32), device, 4-byte aligned
+ * The decode matvec of the pages' runtimes (aot-llm README, Metal backend
+ * notes: matrix-vector kernels with f32 activations and weights dequantized
+ * on the fly; batched prompt notes: each weight decoded once for several
+ * activations).  Any batch >= 1 is accepted; up to 8 vectors share one pass
+ * over W.
+ * Errors: FORMAT, SHAPE, NULL, ALIGN, DTYPE, UNSUPPORTED, OVERFLOW, DEVICE, LAUNCH.
+ */
+int qmv_matvec(int fmt, int64_t N, int64_t K, int64_t batch, const void* W,
+               const void* x, int x_dtype, void* y, int y_dtype, void* stream);
+
+/*
+ * Y[m][n] = sum_k X[m][k] * W[n][k] for m < M, on bf16 matrix cores with f32
+ * accumulation; weight tiles are dequantized once per tile into LDS (aot-llm
+ * README, Metal backend notes: prompt batches use a tiled GEMM on the matrix
+ * units with the weights dequantized once per tile).
+ *   fmt   QMV_W4A16_G64 (others -> UNSUPPORTED)
+ *   X     [M][K] of x_dtype QMV_BF16, device, 16-byte aligned
+ *   Y     [M][N] of y_dtype QMV_BF16, device, 4-byte aligned
+ * Errors: FORMAT, SHAPE, NULL, ALIGN, DTYPE, UNSUPPORTED, OVERFLOW, DEVICE, LAUNCH.
+ */
+int qmv_gemm(int fmt, int64_t N, int64_t K, int64_t M, const void* W, const void* X,
+             int x_dtype, void* Y, int y_dtype, void* stream);
+
+/*
+ * Dense f32 dequantization of one packed matrix into out [N][K] (device),
+ * bit-exact to the definitions above (the correctness baseline's dense
+ * conversion, pytensor-ml issue 53, PR 15 item F-41).  A test/inspection
+ * export: the hot path never calls it.
+ * Errors: FORMAT, SHAPE, NULL, ALIGN, OVERFLOW, DEVICE, LAUNCH.
+ */
+int qmv_dequant(int fmt, int64_t N, int64_t K, const void* W, float* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMV_H_ */

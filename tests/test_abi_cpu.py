@@ -1,0 +1,105 @@
+"""Host-side checks of libqmv (no GPU): the library loads, exports every entry
+point its header declares, sizes packed buffers like the reference layout,
+and rejects bad arguments before touching a device."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmv.h")
+
+
+@pytest.fixture(scope="module")
+def q():
+    import gemm_dequant_matvec_amd as mod
+    return mod
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qmv_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(
+        ["qmv_abi_version", "qmv_status_string", "qmv_last_error", "qmv_packed_bytes",
+         "qmv_pack", "qmv_matvec", "qmv_gemm", "qmv_dequant"])
+
+
+def test_library_exports_every_declared_symbol(q):
+    lib = ctypes.CDLL(q.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(q.EXPORTS) == set(declared_functions())
+
+
+def test_abi_and_status_strings(q):
+    assert q.abi_version() == (1, 1)
+    for st in range(0, -10, -1):
+        assert q._lib.qmv_status_string(st).decode() not in ("", "unknown status")
+    assert q._lib.qmv_status_string(-99).decode() == "unknown status"
+
+
+@pytest.mark.parametrize("fmt", wl.FORMATS)
+@pytest.mark.parametrize("N,mult,batch", [(1, 1, 1), (7, 3, 2), (300, 8, 1), (5632, 8, 3)])
+def test_packed_bytes_matches_reference_layout(q, fmt, N, mult, batch):
+    K = wl.BLOCK[fmt] * mult
+    assert q.packed_bytes(fmt, N, K, batch) == oracle.packed_bytes_ref(fmt, N, K, batch)
+
+
+def test_packed_bytes_errors(q):
+    out = ctypes.c_size_t(0)
+    assert q.raw_call("qmv_packed_bytes", 9, 4, 32, 1, ctypes.byref(out)) == -2
+    assert q.raw_call("qmv_packed_bytes", 1, 0, 32, 1, ctypes.byref(out)) == -4
+    assert q.raw_call("qmv_packed_bytes", 1, 4, 33, 1, ctypes.byref(out)) == -4
+    assert "multiple" in q.last_error()
+    assert q.raw_call("qmv_packed_bytes", 3, 4, 128, 1, ctypes.byref(out)) == -4
+    assert q.raw_call("qmv_packed_bytes", 1, 4, 32, 0, ctypes.byref(out)) == -4
+    assert q.raw_call("qmv_packed_bytes", 1, 4, 32, 1, None) == -1
+    assert q.raw_call("qmv_packed_bytes", 1, 1 << 40, 1 << 40, 1, ctypes.byref(out)) == -7
+
+
+def test_matvec_argument_errors_before_any_launch(q):
+    # fake, aligned, never dereferenced pointers: every case fails on the host
+    P = 1 << 20
+    F32, F16, BF16 = 1, 2, 3
+    call = lambda *a: q.raw_call("qmv_matvec", *a)  # noqa: E731
+    assert call(0, 8, 256, 1, P, P, F32, P, F32, None) == -2
+    assert call(3, 8, 200, 1, P, P, F32, P, F32, None) == -4
+    assert call(3, 8, 256, 0, P, P, F32, P, F32, None) == -4
+    assert call(3, 8, 256, 1, None, P, F32, P, F32, None) == -1
+    assert "W" in q.last_error()
+    assert call(3, 8, 256, 1, P, None, F32, P, F32, None) == -1
+    assert call(3, 8, 256, 1, P, P, 7, P, F32, None) == -6
+    assert call(3, 8, 256, 1, P, P, F16, P, F32, None) == -3      # q4k takes f32 x
+    assert call(2, 8, 256, 1, P, P, BF16, P, F32, None) == -3
+    assert call(2, 8, 256, 1, P, P, F16, P, F16, None) == -3      # y is f32 only
+    assert call(3, 8, 256, 1, P + 4, P, F32, P, F32, None) == -5
+    assert call(3, 8, 256, 1, P, P + 8, F32, P, F32, None) == -5
+    assert call(3, 8, 256, 1, P, P, F32, P + 2, F32, None) == -5
+
+
+def test_gemm_and_pack_argument_errors(q):
+    P = 1 << 20
+    BF16 = 3
+    assert q.raw_call("qmv_gemm", 3, 64, 256, 16, P, P, BF16, P, BF16, None) == -3
+    assert "W4A16" in q.last_error()
+    assert q.raw_call("qmv_gemm", 2, 64, 256, 16, P, P, 1, P, BF16, None) == -3
+    assert q.raw_call("qmv_gemm", 2, 64, 100, 16, P, P, BF16, P, BF16, None) == -4
+    assert q.raw_call("qmv_gemm", 2, 64, 256, 0, P, P, BF16, P, BF16, None) == -4
+    src = q.QmvLogical()
+    src.q = P
+    assert q.raw_call("qmv_pack", 3, 8, 256, 1, ctypes.byref(src), P, None) == -1  # aux NULL
+    assert "aux[0]" in q.last_error()
+    for i in range(4):
+        src.aux[i] = P
+    assert q.raw_call("qmv_pack", 3, 8, 256, 1, None, P, None) == -1
+    assert q.raw_call("qmv_pack", 3, 8, 256, 1, ctypes.byref(src), P + 8, None) == -5
+    assert q.raw_call("qmv_dequant", 4, 8, 256, P, P + 4, None) == -5

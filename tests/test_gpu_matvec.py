@@ -1,0 +1,224 @@
+"""GPU parity of the HIP pack / dequant / matvec path against the CPU oracle.
+
+Bar: packing and dequantization bit-exact; one-hot matvec bit-exact (the
+dequantized column); every matvec output within 1e-3 * ||W_row|| * ||x||.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from gpu_helpers import check_matvec, dev, dev_x, pack_dev, x_values
+
+pytestmark = pytest.mark.gpu
+
+XDT = {"q8_0": ("f32",), "w4a16_g64": ("f16", "f32"), "q4k": ("f32",), "q6k": ("f32",)}
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+# --------------------------------------------------------------- pack/dequant
+
+@pytest.mark.parametrize("fmt", wl.FORMATS)
+@pytest.mark.parametrize("N,mult", [(1, 1), (5, 3), (67, 2)])
+def test_pack_bytes_equal_reference(qmv, fmt, N, mult):
+    K = wl.BLOCK[fmt] * mult
+    w = wl.gen_weights(fmt, N, K, (11, N, mult))
+    _say("pack", fmt, N, K)
+    got = pack_dev(qmv, fmt, w).cpu().numpy()
+    want = oracle.pack_ref(fmt, w)
+    # padding bytes between planes are unspecified; compare the planes only
+    from oracle import layout
+    for name, (off, nb) in layout.plane_offsets(fmt, N, K).items():
+        assert np.array_equal(got[off:off + nb], want[off:off + nb]), name
+    back = oracle.unpack_ref(fmt, N, K, got)
+    for k in w:
+        assert np.array_equal(back[k], w[k]), k
+
+
+@pytest.mark.parametrize("fmt", wl.FORMATS)
+def test_pack_stacked_batch(qmv, fmt):
+    N, K, B = 9, wl.BLOCK[fmt] * 2, 3
+    ws = [wl.gen_weights(fmt, N, K, (12, i, 0)) for i in range(B)]
+    stacked = {k: np.stack([w[k] for w in ws]) for k in ws[0]}
+    d = {k: dev(v) for k, v in stacked.items()}
+    got = qmv.pack(fmt, d, N=N, K=K, batch=B).cpu().numpy()
+    one = qmv.packed_bytes(fmt, N, K)
+    from oracle import layout
+    for i in range(B):
+        want = oracle.pack_ref(fmt, ws[i])
+        for name, (off, nb) in layout.plane_offsets(fmt, N, K).items():
+            assert np.array_equal(got[i * one + off:i * one + off + nb], want[off:off + nb])
+
+
+@pytest.mark.parametrize("fmt", wl.FORMATS)
+@pytest.mark.parametrize("N,mult", [(3, 1), (130, 4)])
+def test_dequant_bit_exact(qmv, fmt, N, mult):
+    K = wl.BLOCK[fmt] * mult
+    w = wl.gen_weights(fmt, N, K, (13, N, mult))
+    _say("dequant", fmt, N, K)
+    Wp = pack_dev(qmv, fmt, w)
+    got = qmv.dequant(fmt, Wp, N, K).cpu().numpy()
+    want = oracle.dequant(fmt, w)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_f16_scale_decode_exhaustive(qmv):
+    """All 65536 fp16 patterns as Q8_0 scales with q = 1: w must be the scale itself."""
+    N, K = 2048, 1024
+    scale = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(N, K // 32)
+    w = {"q": np.ones((N, K), np.int8), "scale": scale}
+    Wp = pack_dev(qmv, "q8_0", w)
+    got = qmv.dequant("q8_0", Wp, N, K).cpu().numpy()[:, ::32].ravel()
+    want = oracle.f16_to_f32(scale.ravel())
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32))
+
+
+def test_q4k_range_edge_and_subnormal_scales(qmv):
+    N, K = 4, 256
+    w = wl.gen_weights("q4k", N, K, (14, 0, 0))
+    w["d"][0, 0], w["dmin"][0, 0] = 0x6400, 0x0001
+    w["sc"][0, :] = 63
+    w["m"][0, :] = 1
+    w["q"][0, :] = 15
+    w["d"][1, 0], w["dmin"][1, 0] = 0x0001, 0x03FF  # subnormals
+    Wp = pack_dev(qmv, "q4k", w)
+    got = qmv.dequant("q4k", Wp, N, K).cpu().numpy()
+    want = oracle.dequant("q4k", w)
+    assert np.all(got[0] == np.float32(967680.0))
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+# ---------------------------------------------------------------- matvec
+
+SHAPES = {  # (N, K) spanning lanes-per-row 16 / 32 / 64, ragged passes and ragged N
+    "q8_0": [(1, 32), (37, 512), (300, 1024), (129, 2560)],
+    "w4a16_g64": [(1, 64), (37, 1024), (300, 2048), (129, 5632)],
+    "q4k": [(1, 256), (37, 1024), (300, 3072), (129, 5632)],
+    "q6k": [(1, 256), (37, 768), (300, 2048), (129, 5632)],
+}
+
+
+@pytest.mark.parametrize("fmt", wl.FORMATS)
+@pytest.mark.parametrize("batch", [1, 2, 3, 8, 11])
+def test_matvec_parity(qmv, fmt, batch):
+    for N, K in SHAPES[fmt]:
+        for xd in XDT[fmt]:
+            w = wl.gen_weights(fmt, N, K, (15, N, K))
+            x = wl.gen_x(K, batch, xd, (15, N, K))
+            _say("matvec", fmt, N, K, batch, xd)
+            r, _, _ = check_matvec(qmv, fmt, w, x, xd)
+            assert r["ok"], (fmt, N, K, batch, xd, r)
+
+
+@pytest.mark.parametrize("fmt", wl.FORMATS)
+def test_one_hot_returns_dequantized_column_bit_exact(qmv, fmt):
+    N, K = 70, wl.BLOCK[fmt] * 8 if fmt != "w4a16_g64" else 2048
+    w = wl.gen_weights(fmt, N, K, (16, 0, 0))
+    W32 = oracle.dequant(fmt, w)
+    Wp = pack_dev(qmv, fmt, w)
+    for xd in XDT[fmt]:
+        ks = [0, 1, 17, 31, 32, 255, K - 1][:8]
+        x = np.zeros((len(ks), K), np.float64)
+        for i, k in enumerate(ks):
+            x[i, k] = 1.0
+        xb = x.astype(np.float32) if xd == "f32" else wl.to_f16_bits(x)
+        y = qmv.matvec(fmt, Wp, dev_x(xb, xd), N, K).cpu().numpy()
+        for i, k in enumerate(ks):
+            assert np.array_equal(y[i], W32[:, k]), (fmt, xd, k)
+
+
+def test_q8_0_minus_128(qmv):
+    N, K = 8, 64
+    w = wl.gen_weights("q8_0", N, K, (17, 0, 0))
+    w["q"][:, ::3] = -128
+    x = wl.gen_x(K, 2, "f32", (17, 0, 0))
+    r, _, _ = check_matvec(qmv, "q8_0", w, x, "f32")
+    assert r["ok"], r
+
+
+@pytest.mark.parametrize("fmt", wl.FORMATS)
+def test_matvec_deterministic(qmv, fmt):
+    N, K = 500, wl.BLOCK[fmt] * 8
+    w = wl.gen_weights(fmt, N, K, (18, 0, 0))
+    xd = XDT[fmt][0]
+    x = dev_x(wl.gen_x(K, 4, xd, (18, 0, 0)), xd)
+    Wp = pack_dev(qmv, fmt, w)
+    a = qmv.matvec(fmt, Wp, x, N, K).cpu().numpy()
+    b = qmv.matvec(fmt, Wp, x, N, K).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_graph_replay_matches_eager(qmv):
+    fmt, N, K = "q4k", 3072, 1024
+    w = wl.gen_weights(fmt, N, K, (19, 0, 0))
+    Wp = pack_dev(qmv, fmt, w)
+    x = dev_x(wl.gen_x(K, 1, "f32", (19, 0, 0)), "f32")
+    eager = qmv.matvec(fmt, Wp, x, N, K).clone()
+    y = torch.empty_like(eager)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        qmv.matvec(fmt, Wp, x, N, K, y=y)
+    for _ in range(3):
+        y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, eager)
+
+
+# ------------------------------------------------------- full workload shapes
+
+def _sample_rows(N, n=384, seed=0):
+    g = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, N - 1], g.integers(0, N, n)]))
+
+
+def test_config_q8_0_512(qmv):
+    c = wl.c1_q8_0()
+    for name, fmt, N, K, key in c["mats"]:
+        w = wl.gen_weights(fmt, N, K, key)
+        x = wl.gen_x(K, c["batch"], c["x_dtype"], key)
+        r, _, _ = check_matvec(qmv, fmt, w, x, c["x_dtype"])
+        _say(name, r)
+        assert r["ok"], r
+
+
+def test_config_w4a16_mlp(qmv):
+    c = wl.c2_w4a16_mlp()
+    for name, fmt, N, K, key in c["mats"]:
+        w = wl.gen_weights(fmt, N, K, key)
+        x = wl.gen_x(K, c["batch"], c["x_dtype"], key)
+        r, _, _ = check_matvec(qmv, fmt, w, x, c["x_dtype"])
+        _say(name, r)
+        assert r["ok"], r
+
+
+def test_config_q4k_mlp_and_vocab_head(qmv):
+    c = wl.c3_q4k_0b6()
+    for name, fmt, N, K, key in c["mats"]:
+        w = wl.gen_weights(fmt, N, K, key)
+        x = wl.gen_x(K, c["batch"], c["x_dtype"], key)
+        rows = _sample_rows(N) if N > 20000 else None
+        r, _, _ = check_matvec(qmv, fmt, w, x, c["x_dtype"], rows=rows)
+        _say(name, r)
+        assert r["ok"], r
+
+
+@pytest.mark.parametrize("batch", [1, 8])
+def test_config_decode_sweep_layer_and_head(qmv, batch):
+    c = wl.c5_sweep(batch, layers=1)
+    for name, fmt, N, K, key in c["mats"]:
+        w = wl.gen_weights(fmt, N, K, key)
+        x = wl.gen_x(K, batch, "f32", key)
+        rows = _sample_rows(N) if N > 20000 else None
+        r, _, _ = check_matvec(qmv, fmt, w, x, "f32", rows=rows)
+        _say(name, batch, r)
+        assert r["ok"], (name, r)
