@@ -109,7 +109,7 @@ def gen_x(K: int, batch: int, dtype: str, key: tuple) -> np.ndarray:
 
 # --------------------------------------------------------------------------
 # Workload tables.  Each matrix: (name, fmt, N, K, key).  Keys are
-# (config id, layer, matrix index); layer -1 marks matrices outside layers.
+# (config id, layer, matrix index); layer 1000 marks matrices outside layers.
 
 LLAMA_1B1 = dict(dim=2048, mlp=5632, layers=22, heads=32, kv_heads=4, head_dim=64, vocab=32000)
 
@@ -134,7 +134,7 @@ def c3_q4k_0b6():
     return dict(name="q4k 0.6B MLP+head b1", x_dtype="f32", batch=1,
                 mats=[("up", "q4k", 3072, 1024, (3, 0, 5)),
                       ("down", "q4k", 1024, 3072, (3, 0, 6)),
-                      ("head", "q4k", 151936, 1024, (3, -1, 7))])
+                      ("head", "q4k", 151936, 1024, (3, 1000, 7))])
 
 
 def c4_gemm(M: int):
@@ -155,7 +155,7 @@ def c5_sweep(batch: int, layers: int = 22):
     for L in range(layers):
         for i, (nm, fmt, N, K) in enumerate(C5_LAYER):
             mats.append((f"l{L}.{nm}", fmt, N, K, (5, L, i)))
-    mats.append(("head", "q6k", LLAMA_1B1["vocab"], LLAMA_1B1["dim"], (5, -1, 7)))
+    mats.append(("head", "q6k", LLAMA_1B1["vocab"], LLAMA_1B1["dim"], (5, 1000, 7)))
     return dict(name=f"1.1B decode sweep b{batch}", x_dtype="f32", batch=batch, mats=mats)
 
 
