@@ -1,0 +1,349 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused dequantize-and-multiply hot path on one MI355X.
+
+Headline (one JSON line on stdout): decode matvec throughput in achieved GB/s
+of algorithmic bytes, on the group-64 W4A16 MLP matvecs of a 1.1B-parameter
+decoder (gate / up 5632 x 2048, down 2048 x 5632, batch 1, fp16 activations).
+A step is one decode token's MLP matvecs over `--copies` distinct weight sets
+(default 32, 623 MB), so every step streams its weights from HBM rather than
+from the 256 MB Infinity Cache; the 3 x copies launches are captured once in a
+HIP graph and replayed.  Inputs are resident in HBM before timing starts.
+
+Algorithmic bytes of one matvec = packed weights including scales / zeros
+(4.5 bits per weight) + activations read + outputs written; the dense
+matrix the method never forms is not counted.  Per the pages' roofline
+method (zynfer PR 100, stage M1/M2 profile notes: bytes per token against
+streamed bandwidth), GB/s = bytes / time.
+
+Also reported (`extras`): single-launch and cold-stream rates of the other
+workloads (Q8_0 512x512, Q4K 0.6B MLP and 151936-row vocab head, the full
+155-matvec 1.1B decode sweep at batch 1 and 8, the W4A16 prefill GEMM at
+M = 16 / 128 / 512 in TFLOP/s), a plain-copy bandwidth probe, and the CPU
+oracle timed on the host (`cpu_baseline`).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--copies C]
+                       [--no-extras] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--copies", type=int, default=32)
+    p.add_argument("--no-extras", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target CPU time of the oracle sample")
+    return p.parse_args()
+
+
+# ----------------------------------------------------------------- helpers
+
+def _dev(a):
+    import numpy as np
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).cuda()
+
+
+def _x_dev(x, dtype):
+    import torch
+    t = _dev(x)
+    return t if dtype == "f32" else t.view(torch.float16 if dtype == "f16" else torch.bfloat16)
+
+
+def matvec_bytes(fmt, N, K, batch, x_bytes_per_el):
+    import workloads as wl
+    return int(round(wl.bytes_per_weight(fmt) * N * K)) + batch * K * x_bytes_per_el + batch * N * 4
+
+
+def time_graph(fn, steps, warmup, stream=None):
+    """Capture fn() once into a HIP graph, replay warmup + steps times; ms per replay."""
+    import torch
+    s = stream or torch.cuda.Stream()
+    fn()  # eager once (argument checks, lazy init)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        fn()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(s)
+        for _ in range(steps):
+            g.replay()
+        t1.record(s)
+    t1.synchronize()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps, g
+
+
+class Stream:
+    """A set of distinct packed copies of some matrices, with per-copy x / y buffers."""
+
+    def __init__(self, qmv, mats, x_dtype, batch, copies):
+        import workloads as wl
+        self.qmv, self.mats, self.x_dtype, self.batch = qmv, mats, x_dtype, batch
+        self.logical = {}
+        self.items = []  # (fmt, N, K, W, x, y)
+        packed = {}
+        for name, fmt, N, K, key in mats:
+            w = wl.gen_weights(fmt, N, K, key)
+            self.logical[name] = (fmt, w, wl.gen_x(K, batch, x_dtype, key))
+            packed[name] = qmv.pack(fmt, {k: _dev(v) for k, v in w.items()})
+        for c in range(copies):
+            for name, fmt, N, K, key in mats:
+                W = packed[name] if c == 0 else packed[name].clone()
+                x = _x_dev(wl.gen_x(K, batch, x_dtype, (key[0], key[1], key[2], 77, c)), x_dtype)
+                y = self._out(N)
+                self.items.append((fmt, N, K, W, x, y))
+        xb = {"f32": 4, "f16": 2, "bf16": 2}[x_dtype]
+        self.bytes = sum(matvec_bytes(f, N, K, batch, xb) for f, N, K, *_ in self.items)
+        self.launches = len(self.items)
+
+    def _out(self, N):
+        import torch
+        return torch.empty((self.batch, N), dtype=torch.float32, device="cuda")
+
+    def __call__(self):
+        mv = self.qmv.matvec
+        for fmt, N, K, W, x, y in self.items:
+            mv(fmt, W, x, N, K, y=y)
+
+
+# ------------------------------------------------------------------ legs
+
+def headline(qmv, args):
+    import workloads as wl
+    c2 = wl.c2_w4a16_mlp()
+    st = Stream(qmv, c2["mats"], c2["x_dtype"], 1, args.copies)
+    ms, _ = time_graph(st, args.steps, args.warmup)
+    gbs = st.bytes / (ms * 1e-3) / 1e9
+    return st, ms, gbs
+
+
+def kernel_leg(qmv, st, steps, warmup):
+    """Per-launch duration of each matvec shape of the headline stream: a graph of
+    back-to-back launches of that shape over all its cold copies, timed with events."""
+    out = {}
+    for name, fmt, N, K, key in st.mats:
+        items = [it for it in st.items if (it[1], it[2]) == (N, K)]
+        # shapes shared by two names (gate/up) are timed once
+        tag = f"{fmt} {N}x{K}"
+        if tag in out:
+            continue
+
+        def run(items=items):
+            for f, n, k, W, x, y in items:
+                qmv.matvec(f, W, x, n, k, y=y)
+        ms, _ = time_graph(run, steps, warmup)
+        per = ms / len(items)
+        b = matvec_bytes(fmt, N, K, 1, 2)
+        out[tag] = {"us_per_launch": per * 1e3, "bytes_per_launch": b,
+                    "gbs": b / (per * 1e-3) / 1e9, "launches": len(items)}
+    return out
+
+
+def copy_probe():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(10):
+        b.copy_(a)
+    t1.record()
+    t1.synchronize()
+    ms = t0.elapsed_time(t1) / 10
+    del a, b
+    return {"bytes": 2 * n, "gbs": 2 * n / (ms * 1e-3) / 1e9, "what": "torch copy_ of 1 GiB (read+write)"}
+
+
+def extras(qmv, args):
+    import workloads as wl
+    res = {}
+    # Q8_0 512x512: one launch, latency-bound
+    c1 = wl.c1_q8_0()
+    st = Stream(qmv, c1["mats"], "f32", 1, 1)
+    ms, _ = time_graph(st, 200, 20)
+    res["q8_0_512x512_b1_single"] = {"us": ms * 1e3, "gbs": st.bytes / (ms * 1e-3) / 1e9}
+    del st
+    # Q4K 0.6B MLP (cold, 170 copies of each = 608 MB) and the vocab head (8 copies = 705 MB)
+    c3 = wl.c3_q4k_0b6()
+    mlp = [m for m in c3["mats"] if m[0] != "head"]
+    st = Stream(qmv, mlp, "f32", 1, 170)
+    ms, _ = time_graph(st, 10, 3)
+    res["q4k_0.6B_mlp_b1_cold"] = {"us_per_launch": ms * 1e3 / st.launches,
+                                   "gbs": st.bytes / (ms * 1e-3) / 1e9, "launches": st.launches}
+    del st
+    head = [m for m in c3["mats"] if m[0] == "head"]
+    st = Stream(qmv, head, "f32", 1, 8)
+    ms, _ = time_graph(st, 10, 3)
+    res["q4k_vocab_head_151936x1024_b1_cold"] = {"us_per_launch": ms * 1e3 / st.launches,
+                                                 "gbs": st.bytes / (ms * 1e-3) / 1e9}
+    del st
+    # full decode sweep of the 1.1B decoder, batch 1 and 8 (155 matvecs, 667 MB of weights)
+    for b in (1, 8):
+        c5 = wl.c5_sweep(b)
+        st = Sweep(qmv, c5, b)
+        ms, _ = time_graph(st, 10, 3)
+        res[f"decode_sweep_1.1B_b{b}"] = {
+            "ms_per_token_step": ms, "tok_per_s": b / (ms * 1e-3),
+            "gbs": st.bytes / (ms * 1e-3) / 1e9, "bytes": st.bytes, "launches": st.launches}
+        del st
+    # prefill GEMM
+    for M in (16, 128, 512):
+        try:
+            res[f"gemm_w4a16_M{M}"] = gemm_leg(qmv, M)
+        except Exception as e:  # GEMM not available: report, do not fake
+            res[f"gemm_w4a16_M{M}"] = {"error": str(e)[:200]}
+    return res
+
+
+class Sweep(Stream):
+    """The 155 matvecs of one decode token: distinct shapes generated once, every
+    layer gets its own device copy (so the 667 MB sweep streams from HBM)."""
+
+    def __init__(self, qmv, cfg, batch):
+        import workloads as wl
+        self.qmv, self.batch = qmv, batch
+        shapes = {}
+        self.items = []
+        for name, fmt, N, K, key in cfg["mats"]:
+            tag = (fmt, N, K)
+            if tag not in shapes:
+                w = wl.gen_weights(fmt, N, K, key)
+                shapes[tag] = qmv.pack(fmt, {k: _dev(v) for k, v in w.items()})
+                W = shapes[tag]
+            else:
+                W = shapes[tag].clone()
+            x = _x_dev(wl.gen_x(K, batch, "f32", key), "f32")
+            self.items.append((fmt, N, K, W, x, self._out(N)))
+        self.bytes = sum(matvec_bytes(f, N, K, batch, 4) for f, N, K, *_ in self.items)
+        self.launches = len(self.items)
+
+
+def gemm_leg(qmv, M):
+    import torch
+    import workloads as wl
+    c4 = wl.c4_gemm(M)
+    name, fmt, N, K, key = c4["mats"][0]
+    w = wl.gen_weights(fmt, N, K, key)
+    W = qmv.pack(fmt, {k: _dev(v) for k, v in w.items()})
+    X = _x_dev(wl.gen_x(K, M, "bf16", key), "bf16")
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ms, _ = time_graph(lambda: qmv.gemm(fmt, W, X, N, K, Y=Y), 50, 10)
+    flops = 2.0 * M * N * K
+    tf = flops / (ms * 1e-3) / 1e12
+    # the matvec path run at batch = M, for the crossover
+    Xf = torch.from_numpy(__import__("oracle").bf16_to_f32(wl.gen_x(K, M, "bf16", key))).cuda()
+    ymv = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ms_mv, _ = time_graph(lambda: qmv.matvec(fmt, W, Xf, N, K, y=ymv), 20, 5)
+    return {"us": ms * 1e3, "tflops": tf, "frac_bf16_peak": tf / BF16_PEAK_TFLOPS,
+            "matvec_path_us": ms_mv * 1e3}
+
+
+def cpu_baseline(st, seconds):
+    """The oracle, untuned, on the host: f32 dequantization + f64 product of the
+    headline matrices (copy 0), repeated until about `seconds` of CPU work."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        blas = 1
+    done_bytes, t0, passes = 0, time.perf_counter(), 0
+    while True:
+        for name in st.logical:
+            fmt, w, x = st.logical[name]
+            W = oracle.dequant(fmt, w)
+            xv = oracle.f16_to_f64(x) if st.x_dtype == "f16" else x.astype(np.float64)
+            oracle.matvec_ref(W, xv)
+            N, K = w["q"].shape
+            done_bytes += matvec_bytes(fmt, N, K, 1, 2)
+        passes += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done_bytes / dt / 1e9, "unit": "GB/s", "cores": blas, "kind": "oracle",
+            "sample": f"{passes} pass(es) over gate+up+down (one 1.1B MLP layer, W4A16 g64, b=1): "
+                      f"numpy f32 dequant (1 thread) + f64 matvec (BLAS, {blas} threads), "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(requested --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import gemm_dequant_matvec_amd as qmv
+    assert torch.cuda.is_available(), "no GPU visible"
+    torch.cuda.set_device(0)
+
+    log("headline: W4A16 g64 1.1B MLP matvecs, batch 1, copies", args.copies)
+    st, ms, gbs = headline(qmv, args)
+    log(f"  {ms * 1e3:.1f} us/step, {gbs:.1f} GB/s")
+    kl = kernel_leg(qmv, st, 20, 5)
+    log("  per-shape:", json.dumps(kl))
+    dom_tag = max(kl, key=lambda t: kl[t]["us_per_launch"] * kl[t]["launches"])
+    dom = kl[dom_tag]
+    roofline = {"bound": "hbm", "achieved": dom["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": dom["gbs"] / HBM_PEAK_GBS, "traffic": None,
+                "kernel": f"matvec_kernel W4A16_G64 f16-x {dom_tag}",
+                "us_per_launch": dom["us_per_launch"], "bytes_per_launch": dom["bytes_per_launch"]}
+    out = {
+        "metric": "decode matvec achieved HBM GB/s (% of peak); prefill GEMM TFLOP/s",
+        "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16*f16->f32", "data": "synthetic (seeded, BASELINE shapes/distributions)",
+        "config": {"workload": "W4A16-g64 decode matvec, 1.1B-decoder MLP (gate, up 5632x2048; "
+                               "down 2048x5632), batch 1, fp16 x",
+                   "copies": args.copies, "launches_per_step": st.launches,
+                   "bytes_per_step": st.bytes, "frac_of_peak": gbs / HBM_PEAK_GBS},
+        "roofline": roofline,
+    }
+    if not args.no_extras:
+        log("copy probe")
+        out["copy_probe"] = copy_probe()
+        log("extras")
+        out["extras"] = extras(qmv, args)
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(st, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

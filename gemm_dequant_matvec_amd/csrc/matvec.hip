@@ -335,6 +335,10 @@ hipError_t launch_matvec(int fmt, int64_t N, int64_t K, int64_t batch, const uin
   const Planes p = planes_of(fmt, N, K);
   const bool f16 = (x_dtype == QMV_F16);
   const size_t xel = f16 ? 2 : 4;
+  if (batch == 1) {
+    hipError_t e = hipSuccess;
+    if (launch_matvec_b1(fmt, N, K, W, x, x_dtype, y, s, &e)) return e;
+  }
   for (int64_t b0 = 0; b0 < batch; b0 += 8) {
     const int nb = static_cast<int>(batch - b0 < 8 ? batch - b0 : 8);
     const void* xb = static_cast<const uint8_t*>(x) + b0 * K * xel;

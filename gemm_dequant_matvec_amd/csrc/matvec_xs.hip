@@ -1,0 +1,416 @@
+// Decode matvec for one or two activation vectors, activation-stationary.
+//
+// Same arithmetic as the general matvec kernel (per-unit scales applied in
+// f32 around an integer-weight inner product), organised for HBM streaming:
+//
+//  * Each lane owns a fixed set of 32-weight units of a row (u = l, l + LPR,
+//    ...), so it loads its slice of x once, precomputes the per-unit sums of
+//    x (and, for fp16 W4A16, the fp16 pairs matching the nibble split), and
+//    keeps them in registers for every row it visits.
+//  * A wave walks row groups with a grid stride.  All weight loads of the
+//    next group are issued before the current group is computed (register
+//    double buffering), so each wave keeps two groups of 128-bit loads in
+//    flight and the first loads leave before anything else happens.
+//  * Partial sums are reduced across the LPR lanes of a row with DPP moves
+//    inside 16-lane rows and ds_bpermute only across rows.
+#include <cstdlib>
+
+#include "qmv_internal.h"
+
+namespace qmv {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+
+typedef __attribute__((ext_vector_type(2))) _Float16 half2_t;
+
+__device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
+__device__ __forceinline__ float byte_f32(uint32_t v, int c) {
+  return static_cast<float>((v >> (8 * c)) & 0xFFu);
+}
+__device__ __forceinline__ float sbyte_f32(uint32_t v, int c) {
+  return static_cast<float>(static_cast<int32_t>(v << (24 - 8 * c)) >> 24);
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Weight bytes are read exactly once: load them with the non-temporal hint so
+// they stream through the caches without displacing the activations.
+#ifndef QMV_NT_WEIGHTS
+#define QMV_NT_WEIGHTS 1
+#endif
+__device__ __forceinline__ uint4 ld_w4(const void* p) {
+#if QMV_NT_WEIGHTS
+  const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+#else
+  return *static_cast<const uint4*>(p);
+#endif
+}
+__device__ __forceinline__ uint2 ld_w2(const void* p) {
+#if QMV_NT_WEIGHTS
+  const u32x2 v = __builtin_nontemporal_load(static_cast<const u32x2*>(p));
+  return make_uint2(v.x, v.y);
+#else
+  return *static_cast<const uint2*>(p);
+#endif
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                              0xF, 0xF, false));
+}
+
+// Sum over each 16-lane row with DPP: afterwards every lane of a row holds the
+// row total (rotate by 8, mirror within 8, then swap pairs inside quads).
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<0x128>(v);  // row_ror:8
+  v += dpp<0x141>(v);  // row_half_mirror
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  return v;
+}
+
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
+// Total of v over the LPR lanes of lane group `sub` (64 / LPR groups per wave).
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v, int sub) {
+  v = row16_sum(v);
+  if constexpr (LPR == 64) {
+    return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+  } else if constexpr (LPR == 32) {
+    const float a = lane_f(v, 0) + lane_f(v, 16);
+    const float b = lane_f(v, 32) + lane_f(v, 48);
+    return sub ? b : a;
+  } else {
+    return v;
+  }
+}
+
+// ----------------------------------------------------------- per-format units
+
+template <int FMT>
+struct Raw;
+template <>
+struct Raw<QMV_Q8_0> { uint4 q0, q1; uint32_t sc; };
+template <>
+struct Raw<QMV_W4A16_G64> { uint4 q; uint32_t sz; };
+template <>
+struct Raw<QMV_Q4K> { uint4 q; uint4 meta; };
+template <>
+struct Raw<QMV_Q6K> { uint4 q; uint2 qh; uint32_t s2; uint32_t d; };
+
+struct Geo {  // plane bases and row strides
+  const uint8_t* W;
+  int64_t off1, off2, off3;
+  int K;
+};
+
+template <int FMT>
+__device__ __forceinline__ Raw<FMT> load_raw(const Geo& g, int row, int u) {
+  Raw<FMT> r;
+  const int64_t R = row;
+  const int K = g.K;
+  if constexpr (FMT == QMV_Q8_0) {
+    const uint4* p = reinterpret_cast<const uint4*>(g.W + R * K) + 2 * u;
+    r.q0 = ld_w4(p);
+    r.q1 = ld_w4(p + 1);
+    r.sc = reinterpret_cast<const uint16_t*>(g.W + g.off1)[R * (K >> 5) + u];
+  } else if constexpr (FMT == QMV_W4A16_G64) {
+    r.q = ld_w4(reinterpret_cast<const uint4*>(g.W + R * (K >> 1)) + u);
+    r.sz = reinterpret_cast<const uint32_t*>(g.W + g.off1)[R * (K >> 6) + (u >> 1)];
+  } else if constexpr (FMT == QMV_Q4K) {
+    r.q = ld_w4(reinterpret_cast<const uint4*>(g.W + R * (K >> 1)) + u);
+    r.meta = reinterpret_cast<const uint4*>(g.W + g.off1)[R * (K >> 8) + (u >> 3)];
+  } else {
+    r.q = ld_w4(reinterpret_cast<const uint4*>(g.W + R * (K >> 1)) + u);
+    r.qh = ld_w2(reinterpret_cast<const uint2*>(g.W + g.off1) + R * (K >> 5) + u);
+    r.s2 = reinterpret_cast<const uint16_t*>(g.W + g.off2)[R * (K >> 5) + u];
+    r.d = reinterpret_cast<const uint16_t*>(g.W + g.off3)[R * (K >> 8) + (u >> 3)];
+  }
+  return r;
+}
+
+// Activation slice of one unit, held in registers.
+template <bool H2>
+struct XUnit;
+template <>
+struct XUnit<false> { float v[32]; float s0, s1; };   // s0: sum of all 32 (or first 16), s1: last 16
+template <>
+struct XUnit<true> { half2_t p[16]; float s; };       // pairs (x_{8i+j}, x_{8i+j+4}), sum
+
+template <int FMT, bool XF16>
+__device__ __forceinline__ void load_x(XUnit<FMT == QMV_W4A16_G64 && XF16>& xu, const void* xv, int64_t off,
+                                       bool valid) {
+  if constexpr (FMT == QMV_W4A16_G64 && XF16) {
+    const uint4* xp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(xv) + off);
+    float s = 0.0f;
+    const half2_t one2 = as_h2(0x3C003C00u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint4 xx = valid ? xp[i] : make_uint4(0, 0, 0, 0);
+      xu.p[4 * i + 0] = as_h2(__builtin_amdgcn_perm(xx.z, xx.x, 0x05040100u));
+      xu.p[4 * i + 1] = as_h2(__builtin_amdgcn_perm(xx.z, xx.x, 0x07060302u));
+      xu.p[4 * i + 2] = as_h2(__builtin_amdgcn_perm(xx.w, xx.y, 0x05040100u));
+      xu.p[4 * i + 3] = as_h2(__builtin_amdgcn_perm(xx.w, xx.y, 0x07060302u));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s = __builtin_amdgcn_fdot2(xu.p[4 * i + j], one2, s, false);
+    }
+    xu.s = s;
+  } else if constexpr (XF16) {
+    const uint4* xp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(xv) + off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint4 xx = valid ? xp[i] : make_uint4(0, 0, 0, 0);
+      const uint32_t w[4] = {xx.x, xx.y, xx.z, xx.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        xu.v[8 * i + 2 * c] = f16_bits_to_f32(w[c] & 0xFFFFu);
+        xu.v[8 * i + 2 * c + 1] = f16_bits_to_f32(w[c] >> 16);
+      }
+    }
+  } else {
+    const float4* xp = reinterpret_cast<const float4*>(static_cast<const float*>(xv) + off);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float4 xx = valid ? xp[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      xu.v[4 * i] = xx.x; xu.v[4 * i + 1] = xx.y; xu.v[4 * i + 2] = xx.z; xu.v[4 * i + 3] = xx.w;
+    }
+  }
+  if constexpr (!(FMT == QMV_W4A16_G64 && XF16)) {
+    float a = 0.f, b = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { a += xu.v[i]; b += xu.v[16 + i]; }
+    if (FMT == QMV_Q6K) { xu.s0 = a; xu.s1 = b; } else { xu.s0 = a + b; xu.s1 = 0.f; }
+  }
+}
+
+// acc += contribution of one unit of one row.  `sh` = 6 * (sub-block index within
+// the Q4K super-block) for the sc / m fields.
+template <int FMT, bool XF16>
+__device__ __forceinline__ float unit_dot(const Raw<FMT>& w, const XUnit<FMT == QMV_W4A16_G64 && XF16>& xu,
+                                          int sh, float acc) {
+  if constexpr (FMT == QMV_W4A16_G64 && XF16) {
+    float dot = 0.0f;
+    const uint32_t wd[4] = {w.q.x, w.q.y, w.q.z, w.q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // (wd >> 4j) & 0x000F000F = nibbles of k = j and j + 4 of this word, as 1024 + q in fp16
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const half2_t h = as_h2(((wd[i] >> (4 * j)) & 0x000F000Fu) | 0x64006400u);
+        dot = __builtin_amdgcn_fdot2(h, xu.p[4 * i + j], dot, false);
+      }
+    }
+    const float s = f16_bits_to_f32(w.sz & 0xFFFFu);
+    const float zo = 1024.0f + f16_bits_to_f32(w.sz >> 16);  // exact
+    return fmaf(s, fmaf(-zo, xu.s, dot), acc);
+  } else if constexpr (FMT == QMV_Q8_0) {
+    float qx = 0.0f;
+    const uint32_t wd[8] = {w.q0.x, w.q0.y, w.q0.z, w.q0.w, w.q1.x, w.q1.y, w.q1.z, w.q1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qx = fmaf(sbyte_f32(wd[i], c), xu.v[4 * i + c], qx);
+    return fmaf(f16_bits_to_f32(w.sc), qx, acc);
+  } else {
+    float qa = 0.0f, qb = 0.0f;
+    const uint32_t wd[4] = {w.q.x, w.q.y, w.q.z, w.q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t ev = wd[i] & 0x0F0F0F0Fu;         // byte c: q[8i + 2c]
+      uint32_t od = (wd[i] >> 4) & 0x0F0F0F0Fu;  // byte c: q[8i + 2c + 1]
+      if constexpr (FMT == QMV_Q6K) {
+        const uint32_t h = (i >> 1) ? w.qh.y : w.qh.x;
+        const int f = (i & 1) * 2;
+        ev |= ((h >> (2 * f)) & 0x03030303u) << 4;
+        od |= ((h >> (2 * f + 2)) & 0x03030303u) << 4;
+      }
+      float t = (FMT == QMV_Q6K && i >= 2) ? qb : qa;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        t = fmaf(byte_f32(ev, c), xu.v[8 * i + 2 * c], t);
+        t = fmaf(byte_f32(od, c), xu.v[8 * i + 2 * c + 1], t);
+      }
+      if (FMT == QMV_Q6K && i >= 2) qb = t; else qa = t;
+    }
+    if constexpr (FMT == QMV_W4A16_G64) {
+      const float s = f16_bits_to_f32(w.sz & 0xFFFFu), z = f16_bits_to_f32(w.sz >> 16);
+      return fmaf(s, fmaf(-z, xu.s0, qa), acc);
+    } else if constexpr (FMT == QMV_Q4K) {
+      const uint64_t lo = uint64_t(w.meta.y) | (uint64_t(w.meta.z) << 32);
+      const uint64_t hi = uint64_t(w.meta.z >> 16) | (uint64_t(w.meta.w) << 16);
+      const float sc = static_cast<float>(static_cast<uint32_t>(lo >> sh) & 63u);
+      const float m = static_cast<float>(static_cast<uint32_t>(hi >> sh) & 63u);
+      const float ds = f16_bits_to_f32(w.meta.x & 0xFFFFu) * sc;
+      const float dm = f16_bits_to_f32(w.meta.x >> 16) * m;
+      acc = fmaf(ds, qa, acc);
+      return fmaf(-dm, xu.s0, acc);
+    } else {  // Q6K
+      const float d = f16_bits_to_f32(w.d);
+      const float s0 = d * static_cast<float>(static_cast<int8_t>(w.s2 & 0xFFu));
+      const float s1 = d * static_cast<float>(static_cast<int8_t>(w.s2 >> 8));
+      acc = fmaf(s0, fmaf(-32.0f, xu.s0, qa), acc);
+      return fmaf(s1, fmaf(-32.0f, xu.s1, qb), acc);
+    }
+  }
+}
+
+// FMT / XF16: format and activation type; LPR lanes per row; UPL units per lane
+// (covers K = 32 * LPR * UPL, ragged tail masked); R rows per lane group; B vectors.
+template <int FMT, bool XF16, int LPR, int UPL, int R, int B>
+__global__ __launch_bounds__(kThreads) void matvec_xs_kernel(Geo g, const void* __restrict__ xv,
+                                                             float* __restrict__ y, int N, int ngroups) {
+  constexpr bool H2 = (FMT == QMV_W4A16_G64 && XF16);
+  constexpr int RPW = 64 / LPR;
+  const int lane = threadIdx.x & 63;
+  const int sub = lane / LPR;
+  const int l = lane % LPR;
+  const int gw = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int TW = gridDim.x * kWaves;
+  const int U = g.K >> 5;
+
+  int uu[UPL], sh[UPL];
+  bool uv[UPL];
+#pragma unroll
+  for (int j = 0; j < UPL; ++j) {
+    const int u = l + j * LPR;
+    uv[j] = u < U;
+    uu[j] = uv[j] ? u : U - 1;
+    sh[j] = 6 * (uu[j] & 7);
+  }
+
+  int grp = gw;
+  Raw<FMT> cur[R][UPL];
+  auto load_group = [&](Raw<FMT> (&dst)[R][UPL], int gi) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int row = min(gi * (R * RPW) + r * RPW + sub, N - 1);
+#pragma unroll
+      for (int j = 0; j < UPL; ++j) dst[r][j] = load_raw<FMT>(g, row, uu[j]);
+    }
+  };
+  if (grp < ngroups) load_group(cur, grp);
+
+  XUnit<H2> xs[B][UPL];
+#pragma unroll
+  for (int b = 0; b < B; ++b)
+#pragma unroll
+    for (int j = 0; j < UPL; ++j)
+      load_x<FMT, XF16>(xs[b][j], xv, int64_t(b) * g.K + 32 * uu[j], uv[j]);
+
+  for (; grp < ngroups; grp += TW) {
+    Raw<FMT> nxt[R][UPL];
+    const int gn = grp + TW;
+    if (gn < ngroups) load_group(nxt, gn);
+    float acc[R * B];
+#pragma unroll
+    for (int i = 0; i < R * B; ++i) acc[i] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < UPL; ++j) {
+      if (uv[j]) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int b = 0; b < B; ++b)
+            acc[r * B + b] = unit_dot<FMT, XF16>(cur[r][j], xs[b][j], sh[j], acc[r * B + b]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < R * B; ++i) {
+      const float tot = group_sum<LPR>(acc[i], sub);
+      const int r = i / B, b = i % B;
+      const int row = grp * (R * RPW) + r * RPW + sub;
+      if (l == 0 && row < N) y[int64_t(b) * N + row] = tot;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int j = 0; j < UPL; ++j) cur[r][j] = nxt[r][j];
+  }
+}
+
+template <int FMT, bool XF16, int LPR, int UPL, int R>
+hipError_t go(const Geo& g, const void* x, float* y, int N, hipStream_t s) {
+  constexpr int rows_per_group = R * (64 / LPR);
+  const int ngroups = (N + rows_per_group - 1) / rows_per_group;
+  // at most 16 waves per CU on 256 CUs; each wave then walks several groups
+  const int max_blocks = 256 * 16 / kWaves;
+  int blocks = (ngroups + kWaves - 1) / kWaves;
+  if (blocks > max_blocks) blocks = max_blocks;
+  hipLaunchKernelGGL((matvec_xs_kernel<FMT, XF16, LPR, UPL, R, 1>), dim3(blocks), dim3(kThreads), 0, s,
+                     g, x, y, N, ngroups);
+  return hipGetLastError();
+}
+
+template <int FMT, bool XF16, int LPR, int UPL>
+hipError_t pick_r(const Geo& g, const void* x, float* y, int N, int rsel, hipStream_t s) {
+  const int groups_r1 = (N + (64 / LPR) - 1) / (64 / LPR);
+  const int r = rsel ? rsel : (groups_r1 >= 4 * 4096 ? 2 : 1);
+  return r == 2 ? go<FMT, XF16, LPR, UPL, 2>(g, x, y, N, s) : go<FMT, XF16, LPR, UPL, 1>(g, x, y, N, s);
+}
+
+template <int FMT, bool XF16>
+bool dispatch(const Geo& g, const void* x, float* y, int N, int rsel, hipStream_t s, hipError_t* e) {
+  constexpr bool H2 = (FMT == QMV_W4A16_G64 && XF16);
+  const int U = g.K / 32;
+  const int lpr = U >= 64 ? 64 : (U > 16 ? 32 : 16);
+  const int upl = (U + lpr - 1) / lpr;
+  // activation registers per unit: 17 (fp16 pairs) or 34 (f32)
+  if (upl > (H2 ? 4 : 3)) return false;
+  if (lpr == 64) {
+    switch (upl) {
+      case 1: *e = pick_r<FMT, XF16, 64, 1>(g, x, y, N, rsel, s); return true;
+      case 2: *e = pick_r<FMT, XF16, 64, 2>(g, x, y, N, rsel, s); return true;
+      case 3: *e = pick_r<FMT, XF16, 64, 3>(g, x, y, N, rsel, s); return true;
+      default:
+        if constexpr (H2) { *e = pick_r<FMT, XF16, 64, 4>(g, x, y, N, rsel, s); return true; }
+        return false;
+    }
+  }
+  if (lpr == 32) {
+    *e = upl == 1 ? pick_r<FMT, XF16, 32, 1>(g, x, y, N, rsel, s) : pick_r<FMT, XF16, 32, 2>(g, x, y, N, rsel, s);
+    return true;
+  }
+  *e = pick_r<FMT, XF16, 16, 1>(g, x, y, N, rsel, s);
+  return true;
+}
+
+int rows_override() {
+  static const int v = [] {
+    const char* e = getenv("QMV_MATVEC_ROWS");  // A/B tuning only: rows per lane group (1 or 2)
+    const int r = e ? atoi(e) : 0;
+    return (r == 1 || r == 2) ? r : 0;
+  }();
+  return v;
+}
+
+}  // namespace
+
+// Single-vector matvec on the activation-stationary kernels.  Returns false
+// (nothing launched) when the shape needs more activation registers than
+// these kernels hold; the caller then uses the general kernel.
+bool launch_matvec_b1(int fmt, int64_t N, int64_t K, const uint8_t* W, const void* x, int x_dtype,
+                      float* y, hipStream_t s, hipError_t* err) {
+  const Planes p = planes_of(fmt, N, K);
+  const Geo g{W, p.off[1], p.off[2], p.off[3], int(K)};
+  const int rsel = rows_override();
+  const bool f16 = (x_dtype == QMV_F16);
+  switch (fmt) {
+    case QMV_Q8_0: return dispatch<QMV_Q8_0, false>(g, x, y, int(N), rsel, s, err);
+    case QMV_W4A16_G64:
+      return f16 ? dispatch<QMV_W4A16_G64, true>(g, x, y, int(N), rsel, s, err)
+                 : dispatch<QMV_W4A16_G64, false>(g, x, y, int(N), rsel, s, err);
+    case QMV_Q4K: return dispatch<QMV_Q4K, false>(g, x, y, int(N), rsel, s, err);
+    case QMV_Q6K: return dispatch<QMV_Q6K, false>(g, x, y, int(N), rsel, s, err);
+    default: return false;
+  }
+}
+
+}  // namespace qmv
