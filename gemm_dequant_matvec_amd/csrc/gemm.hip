@@ -5,22 +5,37 @@
 // prompt evaluation is compute-bound where decode is memory-bound (aot-llm
 // README, "Batched prompt processing").
 //
-// gfx950 mapping.  A workgroup of 4 waves owns a BN x BM output tile (BN
-// weight rows x BM tokens).  The K loop steps by 64 = one W4A16 group, so
-// every weight row has exactly one (scale, zero) per step.  Each step:
-//   * the packed nibbles of the BN x 64 weight tile are dequantized once, in
-//     f32 (w = s*q - s*z, exact for 4-bit q and fp16 s, z) and rounded to bf16
-//     (v_cvt_pk_bf16_f32, round to nearest even) into LDS;
-//   * the BM x 64 bf16 activation tile is copied into LDS;
-//   * each wave contracts its (BN/WN) x (BM/WM) sub-tile with
-//     v_mfma_f32_16x16x32_bf16, A = weight rows, B = token rows, f32
-//     accumulators in registers.
-// The next step's global loads are issued before the current step's MFMAs
-// (register prefetch), so HBM / L2 latency overlaps the matrix work.  LDS rows
-// are padded by 16 bytes so the 16 lanes reading 16 consecutive rows at the
-// same column hit distinct banks.  The epilogue rounds to bf16 and writes 4
-// consecutive outputs (8 bytes) per lane.
+// gfx950 mapping.  A workgroup of 4 waves owns BN = 4 * 16 * FN weight rows
+// and BM = 16 * FM tokens; each wave owns its own 16 * FN weight rows and all
+// BM tokens, with v_mfma_f32_16x16x32_bf16 (A = weight rows, B = tokens, f32
+// accumulators).  The K loop steps by 128:
+//   * Weights go straight from HBM to registers: lane (row r, group g) loads
+//     one 16-byte unit = 32 consecutive k of its row (k = 32g .. 32g + 31 of the
+//     step) and dequantizes it in f32 (w = s*q - s*z, exact for 4-bit q and
+//     fp16 s, z), rounds to bf16 (v_cvt_pk_bf16_f32, round to nearest even) and
+//     feeds word s as the A operand of MFMA s.  So lane group g of MFMA s covers
+//     k = 32g + 8s .. 32g + 8s + 7: a permutation of the 32 k of one MFMA that
+//     the token operand follows as well, which leaves the contraction unchanged.
+//     Each weight of the tile is dequantized exactly once, by one lane, and
+//     never touches LDS.
+//   * The bf16 token tile goes through LDS (two buffers, one barrier per step),
+//     in 128-byte rows: the 8-k chunk 4g + s of a token row is stored in half
+//     s >> 1 at chunk 4 (s & 1) + (g ^ (row & 3)), so the 4 lane groups of MFMA s
+//     read 4 adjacent chunks of 16 consecutive rows, XOR-swizzled by row -- a
+//     pattern gfx950 serves at close to full LDS bandwidth (measured ~260
+//     B/clk/CU; 144-byte padded rows gave ~110).
+//   * Weight loads for S - 1 steps ahead are in flight (register stages); the
+//     K loop is unrolled in chunks so that no load is pending across a loop
+//     back-edge (the compiler drains every load at such an edge).
+// The epilogue rounds to bf16 and writes 4 consecutive outputs (8 bytes) per lane.
+#include <cstdlib>
+#include <utility>
+
 #include "qmv_internal.h"
+
+#ifndef QMV_GEMM_NT
+#define QMV_GEMM_NT 1  // weights stream through once: keep them from evicting the token tile
+#endif
 
 namespace qmv {
 namespace {
@@ -28,102 +43,113 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native vector: stays in registers
 
 constexpr int kThreads = 256;
-constexpr int BK = 64;             // one W4A16 group per k-step
-constexpr int LDS_STRIDE = BK + 8; // bf16 elements per LDS row (144 bytes)
+constexpr int KS = 128;    // k per step: one 16-byte nibble unit per lane of a 16 x 4 fragment
+constexpr int CHUNK = 16;  // steps per fully unrolled chunk
+
+// Workgroup barrier for LDS traffic only: __syncthreads() would also wait for
+// every outstanding global load (its release fence), draining the weight
+// prefetch.  The memory clobber keeps the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   bf16x2 v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// BN x BM tile, waves arranged WN x WM (WN * WM = 4).
-template <int BN, int BM, int WN, int WM>
+// 8 weights (one 32-bit word of nibbles, k in order) -> bf16x8 A operand.
+__device__ __forceinline__ bf16x8 dequant8(uint32_t wd, float s, float c) {
+  uint32_t o[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const uint32_t byte = (wd >> (8 * b)) & 0xFFu;  // k = 2b (low nibble), 2b + 1 (high)
+    o[b] = pack_bf16x2(fmaf(s, static_cast<float>(byte & 15u), c), fmaf(s, static_cast<float>(byte >> 4), c));
+  }
+  return __builtin_bit_cast(bf16x8, u32x4{o[0], o[1], o[2], o[3]});
+}
+
+template <int FN, int FM, int S>
 __global__ __launch_bounds__(kThreads) void gemm_w4g64_kernel(
     const uint8_t* __restrict__ Wq, const uint32_t* __restrict__ Wsz, const uint16_t* __restrict__ X,
     uint16_t* __restrict__ Y, int M, int N, int K, int vec_store) {
-  static_assert(WN * WM == 4, "4 waves");
-  constexpr int TN = BN / WN, TM = BM / WM;  // wave tile
-  constexpr int FN = TN / 16, FM = TM / 16;  // 16x16 fragments per wave
-  static_assert(FN * 16 == TN && FM * 16 == TM, "wave tile must be a multiple of 16");
-  constexpr int WTASKS = BN * 2;             // 16-byte nibble chunks (32 weights) per k-step
-  constexpr int WPER = (WTASKS + kThreads - 1) / kThreads;
-  constexpr int XCHUNKS = BM * (BK / 8);     // 16-byte bf16 chunks per k-step
-  constexpr int XPER = (XCHUNKS + kThreads - 1) / kThreads;
+  constexpr int TN = 16 * FN, BN = 4 * TN, BM = 16 * FM;
+  constexpr int XPER = BM * (KS / 8) / kThreads;  // 16-byte token chunks per thread per step
+  static_assert(XPER * kThreads == BM * (KS / 8), "token tile must split evenly");
+  static_assert(S >= 1 && S <= 8, "1..8 weight stages");
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ws[BN * LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) uint16_t Xs[BM * LDS_STRIDE];
+  // [buffer][k half][token row][16-byte chunk]
+  __shared__ u32x4 Xs[2][2][BM][8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wn = wave % WN, wm = wave / WN;
-  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
-  const int nk = K / BK;
-  const int64_t qrow = K / 2;   // nibble bytes per weight row
-  const int64_t grow = K / 64;  // groups per weight row
+  const int fr = lane & 15;  // fragment row: weight row (A) / token row (B)
+  const int g = lane >> 4;   // lane group: 32-k unit within the step
+  const int nw = blockIdx.x * BN + wave * TN;  // first weight row of this wave
+  const int m0 = blockIdx.y * BM;
+  const int nk = (K + KS - 1) / KS;
+  const int64_t qrow = K / 2, grow = K / 64;
+  // Blocks walk K from different starting steps: in lockstep they would all
+  // read the same k offset of rows 4 KiB apart, which lands on the same L2
+  // channels.  Only the order of the f32 accumulation changes.
+  const int krot = (blockIdx.x + 7 * blockIdx.y) % nk;
+  auto kstep = [&](int ks) { const int t = ks + krot; return t >= nk ? t - nk : t; };
 
-  // global -> register staging for one k-step
-  uint4 wq[WPER];
-  uint32_t wsz[WPER];
-  uint4 xr[XPER];
-  auto load_step = [&](int ks) {
+  struct Stage {
+    u32x4 q[FN];       // k = 32g .. 32g + 31 of the step, row nw + 16f + fr
+    uint32_t sz[FN];   // (scale, zero) of that unit's group
+  };
+  Stage s0, s1, s2, s3, s4, s5, s6, s7;  // named, so every stage stays in registers
+  auto stage = [&]<int I>() -> Stage& {
+    constexpr int i = I % S;
+    if constexpr (i == 0) return s0;
+    else if constexpr (i == 1) return s1;
+    else if constexpr (i == 2) return s2;
+    else if constexpr (i == 3) return s3;
+    else if constexpr (i == 4) return s4;
+    else if constexpr (i == 5) return s5;
+    else if constexpr (i == 6) return s6;
+    else return s7;
+  };
+
+  // Loads are unconditional with clamped addresses: a load under a divergent
+  // branch makes the compiler drain all loads at the join.  Rows past N and a
+  // k unit past K read valid duplicates; the latter are zeroed in compute.
+  auto load_w = [&](Stage& st, int ks) {
+    const int ku = min(kstep(ks) * KS + 32 * g, K - 32);  // first k of this lane's unit
 #pragma unroll
-    for (int i = 0; i < WPER; ++i) {
-      const int t = tid + i * kThreads;
-      if (t < WTASKS) {
-        const int r = t >> 1, half = t & 1;
-        const int n = min(n0 + r, N - 1);
-        wq[i] = *reinterpret_cast<const uint4*>(Wq + n * qrow + ks * 32 + half * 16);
-        wsz[i] = Wsz[n * grow + ks];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < XPER; ++i) {
-      const int t = tid + i * kThreads;
-      if (t < XCHUNKS) {
-        const int r = t >> 3, c = t & 7;
-        const int m = m0 + r;
-        xr[i] = m < M ? *reinterpret_cast<const uint4*>(X + int64_t(m) * K + ks * BK + c * 8)
-                      : make_uint4(0, 0, 0, 0);
-      }
+    for (int f = 0; f < FN; ++f) {
+      const int n = min(nw + 16 * f + fr, N - 1);
+#if QMV_GEMM_NT
+      st.q[f] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Wq + n * qrow + ku / 2));
+#else
+      st.q[f] = *reinterpret_cast<const u32x4*>(Wq + n * qrow + ku / 2);
+#endif
+      st.sz[f] = Wsz[n * grow + ku / 64];
     }
   };
-  auto store_step = [&]() {
+  u32x4 xr[XPER];
+  auto load_x = [&](int ks) {
 #pragma unroll
-    for (int i = 0; i < WPER; ++i) {
-      const int t = tid + i * kThreads;
-      if (t < WTASKS) {
-        const int r = t >> 1, half = t & 1;
-        const float s = f16_bits_to_f32(wsz[i] & 0xFFFFu);
-        const float c = -(s * f16_bits_to_f32(wsz[i] >> 16));
-        const uint32_t wd[4] = {wq[i].x, wq[i].y, wq[i].z, wq[i].w};
-        uint32_t o[16];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          // byte b of wd[j] holds k = 8j + 2b (low nibble) and 8j + 2b + 1 (high nibble)
-          float w[8];
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const uint32_t byte = (wd[j] >> (8 * b)) & 0xFFu;
-            w[2 * b] = fmaf(s, static_cast<float>(byte & 15u), c);
-            w[2 * b + 1] = fmaf(s, static_cast<float>(byte >> 4), c);
-          }
-#pragma unroll
-          for (int p = 0; p < 4; ++p) o[4 * j + p] = pack_bf16x2(w[2 * p], w[2 * p + 1]);
-        }
-        uint4* dst = reinterpret_cast<uint4*>(Ws + r * LDS_STRIDE + half * 32);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) dst[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
-      }
+    for (int p = 0; p < XPER; ++p) {
+      const int id = p * kThreads + tid;
+      const int r = id >> 4, c16 = id & 15;
+      const int m = min(m0 + r, M - 1);
+      const int k = min(kstep(ks) * KS + 8 * c16, K - 8);
+      xr[p] = *reinterpret_cast<const u32x4*>(X + int64_t(m) * K + k);
     }
+  };
+  auto store_x = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < XPER; ++i) {
-      const int t = tid + i * kThreads;
-      if (t < XCHUNKS) {
-        const int r = t >> 3, c = t & 7;
-        *reinterpret_cast<uint4*>(Xs + r * LDS_STRIDE + c * 8) = xr[i];
-      }
+    for (int p = 0; p < XPER; ++p) {
+      const int id = p * kThreads + tid;
+      const int r = id >> 4, c16 = id & 15;
+      const int gg = c16 >> 2, ss = c16 & 3;  // k = 32 gg + 8 ss
+      Xs[buf][ss >> 1][r][4 * (ss & 1) + (gg ^ (r & 3))] = xr[p];
     }
   };
 
@@ -133,41 +159,79 @@ __global__ __launch_bounds__(kThreads) void gemm_w4g64_kernel(
 #pragma unroll
     for (int b = 0; b < FM; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int fr = lane & 15;        // fragment row (weight row for A, token row for B)
-  const int fk = (lane >> 4) * 8;  // this lane's 8 k values inside a 32-wide chunk
-
-  load_step(0);
-  for (int ks = 0; ks < nk; ++ks) {
-    store_step();
-    __syncthreads();
-    if (ks + 1 < nk) load_step(ks + 1);
+  auto compute = [&](const Stage& st, int ks) {
+    const bool kin = kstep(ks) * KS + 32 * g < K;  // false only in a trailing half step
+    float sc[FN], cz[FN];
 #pragma unroll
-    for (int kc = 0; kc < BK / 32; ++kc) {
-      bf16x8 a[FN], b[FM];
-#pragma unroll
-      for (int i = 0; i < FN; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(Ws + (wn * TN + i * 16 + fr) * LDS_STRIDE + kc * 32 + fk);
+    for (int f = 0; f < FN; ++f) {
+      sc[f] = f16_bits_to_f32(st.sz[f] & 0xFFFFu);
+      cz[f] = -(sc[f] * f16_bits_to_f32(st.sz[f] >> 16));
+      if (!kin) sc[f] = cz[f] = 0.0f;
+    }
+    const int buf = ks & 1;
+    // B fragments of slice s + 1 are read while slice s runs on the matrix
+    // cores; without the scheduling fences the compiler issues each read right
+    // before its MFMA and every MFMA waits out a full LDS latency.
+    auto read_b = [&](bf16x8 (&b)[FM], int s) {
 #pragma unroll
       for (int j = 0; j < FM; ++j)
-        b[j] = *reinterpret_cast<const bf16x8*>(Xs + (wm * TM + j * 16 + fr) * LDS_STRIDE + kc * 32 + fk);
+        b[j] = __builtin_bit_cast(bf16x8, Xs[buf][s >> 1][16 * j + fr][4 * (s & 1) + (g ^ (fr & 3))]);
+    };
+    bf16x8 b0[FM], b1[FM];
+    read_b(b0, 0);
 #pragma unroll
-      for (int i = 0; i < FN; ++i)
+    for (int s = 0; s < 4; ++s) {
+      bf16x8 (&cur)[FM] = (s & 1) ? b1 : b0;
+      bf16x8 (&nxt)[FM] = (s & 1) ? b0 : b1;
+      if (s < 3) read_b(nxt, s + 1);
+      bf16x8 a[FN];
+#pragma unroll
+      for (int f = 0; f < FN; ++f) a[f] = dequant8(st.q[f][s], sc[f], cz[f]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int f = 0; f < FN; ++f)
 #pragma unroll
         for (int j = 0; j < FM; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+          acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[f], cur[j], acc[f][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __syncthreads();
-  }
+  };
 
-  // C[n][m] fragment: lane holds n = 4*(lane/16) + e, m = lane % 16
+  // token tiles: step 0 staged before the loop, step ks + 1 written during step ks
+  load_x(0);
+  store_x(0);
+  if (nk > 1) load_x(1);
+  lds_barrier();
+
+  auto chunk = [&]<int CH>(int c0) {
+    [&]<int... P>(std::integer_sequence<int, P...>) {
+      ((P < CH ? load_w(stage.template operator()<P>(), c0 + P) : void()), ...);
+    }(std::make_integer_sequence<int, (S - 1 < CH ? S - 1 : CH)>{});
+    [&]<int... J>(std::integer_sequence<int, J...>) {
+      (([&] {
+         const int ks = c0 + J;
+         if constexpr (J + S - 1 < CH) load_w(stage.template operator()<J + S - 1>(), ks + S - 1);
+         compute(stage.template operator()<J>(), ks);
+         if (ks + 1 < nk) store_x((ks + 1) & 1);
+         if (ks + 2 < nk) load_x(ks + 2);
+         lds_barrier();
+       }()),
+       ...);
+    }(std::make_integer_sequence<int, CH>{});
+  };
+  int k0 = 0;
+  for (; k0 + CHUNK <= nk; k0 += CHUNK) chunk.template operator()<CHUNK>(k0);
+  for (; k0 < nk; ++k0) chunk.template operator()<1>(k0);
+
+  // C fragment (weight rows x tokens): lane holds n = 4 * (lane / 16) + e, m = lane % 16
 #pragma unroll
-  for (int i = 0; i < FN; ++i) {
-    const int n = n0 + wn * TN + i * 16 + 4 * (lane >> 4);
+  for (int f = 0; f < FN; ++f) {
+    const int n = nw + 16 * f + 4 * g;
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
-      const int m = m0 + wm * TM + j * 16 + (lane & 15);
+      const int m = m0 + 16 * j + fr;
       if (m < M) {
-        const f32x4 v = acc[i][j];
+        const f32x4 v = acc[f][j];
         uint16_t* dst = Y + int64_t(m) * N + n;
         if (vec_store && n + 3 < N) {  // 8-byte aligned: N % 4 == 0 and Y 8-byte aligned
           *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
@@ -181,12 +245,13 @@ __global__ __launch_bounds__(kThreads) void gemm_w4g64_kernel(
   }
 }
 
-template <int BN, int BM, int WN, int WM>
+template <int FN, int FM, int S>
 hipError_t go(const uint8_t* W, const Planes& p, const uint16_t* X, uint16_t* Y, int M, int N, int K,
               hipStream_t s) {
+  constexpr int BN = 64 * FN, BM = 16 * FM;
   const dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM);
   const int vec = (N % 4 == 0) && (reinterpret_cast<uintptr_t>(Y) % 8 == 0);
-  hipLaunchKernelGGL((gemm_w4g64_kernel<BN, BM, WN, WM>), grid, dim3(kThreads), 0, s, W,
+  hipLaunchKernelGGL((gemm_w4g64_kernel<FN, FM, S>), grid, dim3(kThreads), 0, s, W,
                      reinterpret_cast<const uint32_t*>(W + p.off[1]), X, Y, M, N, K, vec);
   return hipGetLastError();
 }
@@ -198,10 +263,27 @@ hipError_t launch_gemm(int fmt, int64_t N, int64_t K, int64_t M, const uint8_t* 
   if (fmt != QMV_W4A16_G64) return hipErrorInvalidValue;
   const Planes p = planes_of(fmt, N, K);
   const int n = int(N), k = int(K), m = int(M);
-  if (m <= 16) return go<64, 16, 4, 1>(W, p, X, Y, m, n, k, s);
-  if (m <= 32) return go<64, 32, 4, 1>(W, p, X, Y, m, n, k, s);
-  if (m <= 128) return go<64, 64, 2, 2>(W, p, X, Y, m, n, k, s);
-  return go<96, 128, 2, 2>(W, p, X, Y, m, n, k, s);
+  // A/B tuning only: QMV_GEMM_TILE forces one of the tile configurations below.
+  static const int forced = [] {
+    const char* e = getenv("QMV_GEMM_TILE");
+    return e ? atoi(e) : -1;
+  }();
+  switch (forced) {
+    case 0: return go<1, 8, 4>(W, p, X, Y, m, n, k, s);
+    case 1: return go<2, 8, 4>(W, p, X, Y, m, n, k, s);
+    case 2: return go<1, 4, 4>(W, p, X, Y, m, n, k, s);
+    case 3: return go<2, 4, 4>(W, p, X, Y, m, n, k, s);
+    case 4: return go<2, 4, 6>(W, p, X, Y, m, n, k, s);
+    case 5: return go<4, 4, 4>(W, p, X, Y, m, n, k, s);
+    case 6: return go<1, 2, 6>(W, p, X, Y, m, n, k, s);
+    case 7: return go<1, 1, 8>(W, p, X, Y, m, n, k, s);
+    case 8: return go<2, 2, 6>(W, p, X, Y, m, n, k, s);
+    default: break;
+  }
+  // measured on MI355X (5632 x 2048): M = 16 -> <1,1,8>, M = 128 and 512 -> <1,4,4>
+  if (m <= 16) return go<1, 1, 8>(W, p, X, Y, m, n, k, s);
+  if (m <= 32) return go<1, 2, 6>(W, p, X, Y, m, n, k, s);
+  return go<1, 4, 4>(W, p, X, Y, m, n, k, s);
 }
 
 }  // namespace qmv
