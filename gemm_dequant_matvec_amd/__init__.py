@@ -4,7 +4,7 @@ weights on MI355X (gfx950).
 Argument marshalling only.  Every step of the computation runs in the HIP
 kernels of libqmv.so; PyTorch supplies device memory and the current stream.
 Importing this package fails loudly when the library has not been built
-(`python -m gemm_dequant_matvec_amd.build`); there is no CPU fallback.
+(`python gemm_dequant_matvec_amd/build.py`); there is no CPU fallback.
 
     import gemm_dequant_matvec_amd as qmv
     W = qmv.pack("q4k", {"q": q, "sc": sc, "m": m, "d": d, "dmin": dmin})
@@ -34,7 +34,7 @@ _DTYPES = {torch.float32: 1, torch.float16: 2, torch.bfloat16: 3}
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"libqmv.so not found at {LIB_PATH}: build it with "
-        "`python -m gemm_dequant_matvec_amd.build` (hipcc, gfx950)")
+        "`python gemm_dequant_matvec_amd/build.py` (hipcc, gfx950)")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -56,13 +56,21 @@ _lib.qmv_pack.argtypes = [_int, _i64, _i64, _i64, ctypes.POINTER(QmvLogical), _v
 _lib.qmv_pack.restype = _int
 _lib.qmv_matvec.argtypes = [_int, _i64, _i64, _i64, _vp, _vp, _int, _vp, _int, _vp]
 _lib.qmv_matvec.restype = _int
+
+
+class QmvMatvecItem(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int64), ("W", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p)]
+
+
+_lib.qmv_matvec_grouped.argtypes = [_int, _i64, _i64, _int, ctypes.POINTER(QmvMatvecItem), _int, _int, _vp]
+_lib.qmv_matvec_grouped.restype = _int
 _lib.qmv_gemm.argtypes = [_int, _i64, _i64, _i64, _vp, _vp, _int, _vp, _int, _vp]
 _lib.qmv_gemm.restype = _int
 _lib.qmv_dequant.argtypes = [_int, _i64, _i64, _vp, _vp, _vp]
 _lib.qmv_dequant.restype = _int
 
 EXPORTS = ("qmv_abi_version", "qmv_status_string", "qmv_last_error", "qmv_packed_bytes",
-           "qmv_pack", "qmv_matvec", "qmv_gemm", "qmv_dequant")
+           "qmv_pack", "qmv_matvec", "qmv_matvec_grouped", "qmv_gemm", "qmv_dequant")
 
 
 class QmvError(RuntimeError):
@@ -144,6 +152,30 @@ def matvec(fmt, W: torch.Tensor, x: torch.Tensor, N: int, K: int, y: torch.Tenso
     _check(_lib.qmv_matvec(_fmt(fmt), N, K, b, _ptr(W), _ptr(x2), _DTYPES[x2.dtype], _ptr(y),
                            _DTYPES[y.dtype], _stream(stream)))
     return y
+
+
+def matvec_grouped(fmt, items, K: int, stream=None) -> list:
+    """Several matvecs of one format and K in as few launches as possible.
+
+    items: sequence of (W, x, N) or (W, x, N, y); x [b][K] (same b and dtype for
+    all), y allocated as f32 [b][N] when absent.  Returns the list of y.
+    """
+    arr = (QmvMatvecItem * len(items))()
+    outs = []
+    b = xdt = None
+    for i, it in enumerate(items):
+        W, x, N = it[0], it[1], it[2]
+        x2 = x if x.dim() == 2 else x.reshape(1, -1)
+        if b is None:
+            b, xdt = x2.shape[0], x2.dtype
+        if x2.shape != (b, K) or x2.dtype != xdt:
+            raise ValueError("all items need x of shape [b][K] and one dtype")
+        y = it[3] if len(it) > 3 else torch.empty((b, N), dtype=torch.float32, device=x.device)
+        arr[i].N, arr[i].W, arr[i].x, arr[i].y = N, _ptr(W), _ptr(x2), _ptr(y)
+        outs.append(y)
+    _check(_lib.qmv_matvec_grouped(_fmt(fmt), K, b, len(items), arr, _DTYPES[xdt], _DTYPES[torch.float32],
+                                   _stream(stream)))
+    return outs
 
 
 def gemm(fmt, W: torch.Tensor, X: torch.Tensor, N: int, K: int, Y: torch.Tensor | None = None,

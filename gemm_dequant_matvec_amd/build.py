@@ -1,6 +1,10 @@
 """Build libqmv.so for gfx950 from csrc/*.hip with hipcc (in-tree).
 
-    python -m gemm_dequant_matvec_amd.build        # or build() from Python
+    python gemm_dequant_matvec_amd/build.py        # or build() from Python
+
+The script stands alone (it imports nothing from the package, whose import
+loads the library it builds), so it also runs when libqmv.so is missing or
+stale.
 
 Every HIP source is compiled with packed-FP32 instructions disabled (the
 compiler would otherwise form v_pk_fma_f32 and friends from scalar code).

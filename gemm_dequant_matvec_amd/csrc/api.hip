@@ -154,14 +154,13 @@ int qmv_pack(int fmt, int64_t N, int64_t K, int64_t batch, const qmv_logical* sr
                   "pack");
 }
 
-int qmv_matvec(int fmt, int64_t N, int64_t K, int64_t batch, const void* W, const void* x,
-               int x_dtype, void* y, int y_dtype, void* stream) {
+static int check_matvec_args(int fmt, int64_t N, int64_t K, int64_t batch, const void* W, const void* x,
+                             int x_dtype, const void* y, int y_dtype, const char* who) {
   int st;
-  if ((st = check_fmt(fmt))) return st;
   if ((st = check_shape(fmt, N, K, batch, "batch"))) return st;
-  if (!W) return fail(QMV_ERR_NULL, "W is NULL");
-  if (!x) return fail(QMV_ERR_NULL, "x is NULL");
-  if (!y) return fail(QMV_ERR_NULL, "y is NULL");
+  if (!W) return fail(QMV_ERR_NULL, "%sW is NULL", who);
+  if (!x) return fail(QMV_ERR_NULL, "%sx is NULL", who);
+  if (!y) return fail(QMV_ERR_NULL, "%sy is NULL", who);
   if (x_dtype != QMV_F32 && x_dtype != QMV_F16 && x_dtype != QMV_BF16)
     return fail(QMV_ERR_DTYPE, "x_dtype=%d is not a qmv_dtype", x_dtype);
   if (y_dtype != QMV_F32 && y_dtype != QMV_F16 && y_dtype != QMV_BF16)
@@ -170,15 +169,50 @@ int qmv_matvec(int fmt, int64_t N, int64_t K, int64_t batch, const void* W, cons
     return fail(QMV_ERR_UNSUPPORTED, "%s matvec takes x as f32%s", fmt_name(fmt),
                 fmt == QMV_W4A16_G64 ? " or f16" : "");
   if (y_dtype != QMV_F32) return fail(QMV_ERR_UNSUPPORTED, "matvec writes y as f32 only");
-  if (!aligned(W, 16)) return fail(QMV_ERR_ALIGN, "W is not 16-byte aligned");
-  if (!aligned(x, 16)) return fail(QMV_ERR_ALIGN, "x is not 16-byte aligned");
-  if (!aligned(y, 4)) return fail(QMV_ERR_ALIGN, "y is not 4-byte aligned");
+  if (!aligned(W, 16)) return fail(QMV_ERR_ALIGN, "%sW is not 16-byte aligned", who);
+  if (!aligned(x, 16)) return fail(QMV_ERR_ALIGN, "%sx is not 16-byte aligned", who);
+  if (!aligned(y, 4)) return fail(QMV_ERR_ALIGN, "%sy is not 4-byte aligned", who);
   const int64_t lim = int64_t(1) << 31;
   if (N * 16 >= lim) return fail(QMV_ERR_OVERFLOW, "N=%lld too large for the row grid", (long long)N);
+  return QMV_OK;
+}
+
+int qmv_matvec(int fmt, int64_t N, int64_t K, int64_t batch, const void* W, const void* x,
+               int x_dtype, void* y, int y_dtype, void* stream) {
+  int st;
+  if ((st = check_fmt(fmt))) return st;
+  if ((st = check_matvec_args(fmt, N, K, batch, W, x, x_dtype, y, y_dtype, ""))) return st;
   if ((st = check_device())) return st;
   return launched(qmv::launch_matvec(fmt, N, K, batch, static_cast<const uint8_t*>(W), x, x_dtype,
                                      static_cast<float*>(y), as_stream(stream)),
                   "matvec");
+}
+
+int qmv_matvec_grouped(int fmt, int64_t K, int64_t batch, int count, const qmv_matvec_item* items,
+                       int x_dtype, int y_dtype, void* stream) {
+  int st;
+  if ((st = check_fmt(fmt))) return st;
+  if (count < 1) return fail(QMV_ERR_SHAPE, "count=%d must be >= 1", count);
+  if (!items) return fail(QMV_ERR_NULL, "items is NULL");
+  char who[32];
+  for (int i = 0; i < count; ++i) {
+    std::snprintf(who, sizeof(who), "items[%d].", i);
+    if ((st = check_matvec_args(fmt, items[i].N, K, batch, items[i].W, items[i].x, x_dtype, items[i].y,
+                                y_dtype, who)))
+      return st;
+  }
+  if ((st = check_device())) return st;
+  hipStream_t s = as_stream(stream);
+  if (batch == 1) {
+    hipError_t e = hipSuccess;
+    if (qmv::launch_matvec_grouped_b1(fmt, K, count, items, x_dtype, s, &e)) return launched(e, "grouped matvec");
+  }
+  for (int i = 0; i < count; ++i) {
+    const hipError_t e = qmv::launch_matvec(fmt, items[i].N, K, batch, static_cast<const uint8_t*>(items[i].W),
+                                            items[i].x, x_dtype, static_cast<float*>(items[i].y), s);
+    if (e != hipSuccess) return launched(e, "grouped matvec");
+  }
+  return ok();
 }
 
 int qmv_gemm(int fmt, int64_t N, int64_t K, int64_t M, const void* W, const void* X, int x_dtype,

@@ -262,11 +262,30 @@ __device__ __forceinline__ float unit_dot(const Raw<FMT>& w, const XUnit<FMT == 
   }
 }
 
+// Up to kMaxSeg matrices of one format and one K per launch.  Each segment is
+// one matvec (its packed planes, x, y, row count) and owns a contiguous range
+// of row groups; the table travels in the kernel arguments (no device copy,
+// so launches stay graph-capturable).
+constexpr int kMaxSeg = 16;
+struct Seg {
+  const uint8_t* W;
+  int64_t off1, off2, off3;
+  const void* x;
+  float* y;
+  int N;
+  int g0;  // first row group of this segment
+};
+struct SegTable {
+  Seg s[kMaxSeg];
+  int count;
+  int ngroups;  // total row groups
+  int K;
+};
+
 // FMT / XF16: format and activation type; LPR lanes per row; UPL units per lane
-// (covers K = 32 * LPR * UPL, ragged tail masked); R rows per lane group; B vectors.
-template <int FMT, bool XF16, int LPR, int UPL, int R, int B>
-__global__ __launch_bounds__(kThreads) void matvec_xs_kernel(Geo g, const void* __restrict__ xv,
-                                                             float* __restrict__ y, int N, int ngroups) {
+// (covers K = 32 * LPR * UPL, ragged tail masked); R rows per lane group.
+template <int FMT, bool XF16, int LPR, int UPL, int R>
+__global__ __launch_bounds__(kThreads) void matvec_xs_kernel(const SegTable t) {
   constexpr bool H2 = (FMT == QMV_W4A16_G64 && XF16);
   constexpr int RPW = 64 / LPR;
   const int lane = threadIdx.x & 63;
@@ -274,7 +293,8 @@ __global__ __launch_bounds__(kThreads) void matvec_xs_kernel(Geo g, const void* 
   const int l = lane % LPR;
   const int gw = blockIdx.x * kWaves + (threadIdx.x >> 6);
   const int TW = gridDim.x * kWaves;
-  const int U = g.K >> 5;
+  const int K = t.K;
+  const int U = K >> 5;
 
   int uu[UPL], sh[UPL];
   bool uv[UPL];
@@ -286,48 +306,55 @@ __global__ __launch_bounds__(kThreads) void matvec_xs_kernel(Geo g, const void* 
     sh[j] = 6 * (uu[j] & 7);
   }
 
-  int grp = gw;
-  Raw<FMT> cur[R][UPL];
+  // segment holding row group gi (wave-uniform scan of at most kMaxSeg entries)
+  auto seg_of = [&](int gi) {
+    int si = 0;
+    for (int i = 1; i < t.count; ++i) si = (gi >= t.s[i].g0) ? i : si;
+    return si;
+  };
   auto load_group = [&](Raw<FMT> (&dst)[R][UPL], int gi) {
+    const Seg& sg = t.s[seg_of(gi)];
+    const Geo geo{sg.W, sg.off1, sg.off2, sg.off3, K};
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int row = min(gi * (R * RPW) + r * RPW + sub, N - 1);
+      const int row = min((gi - sg.g0) * (R * RPW) + r * RPW + sub, sg.N - 1);
 #pragma unroll
-      for (int j = 0; j < UPL; ++j) dst[r][j] = load_raw<FMT>(g, row, uu[j]);
+      for (int j = 0; j < UPL; ++j) dst[r][j] = load_raw<FMT>(geo, row, uu[j]);
     }
   };
-  if (grp < ngroups) load_group(cur, grp);
 
-  XUnit<H2> xs[B][UPL];
-#pragma unroll
-  for (int b = 0; b < B; ++b)
-#pragma unroll
-    for (int j = 0; j < UPL; ++j)
-      load_x<FMT, XF16>(xs[b][j], xv, int64_t(b) * g.K + 32 * uu[j], uv[j]);
+  int grp = gw;
+  if (grp >= t.ngroups) return;  // the whole wave leaves; no block-level barrier follows
+  Raw<FMT> cur[R][UPL];
+  load_group(cur, grp);
 
-  for (; grp < ngroups; grp += TW) {
+  XUnit<H2> xs[UPL];
+  const void* xcur = nullptr;
+  for (; grp < t.ngroups; grp += TW) {
     Raw<FMT> nxt[R][UPL];
     const int gn = grp + TW;
-    if (gn < ngroups) load_group(nxt, gn);
-    float acc[R * B];
+    if (gn < t.ngroups) load_group(nxt, gn);
+    const Seg& sg = t.s[seg_of(grp)];
+    if (sg.x != xcur) {  // a segment with other activations: reload this lane's slice
+      xcur = sg.x;
 #pragma unroll
-    for (int i = 0; i < R * B; ++i) acc[i] = 0.0f;
+      for (int j = 0; j < UPL; ++j) load_x<FMT, XF16>(xs[j], xcur, 32 * uu[j], uv[j]);
+    }
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.0f;
 #pragma unroll
     for (int j = 0; j < UPL; ++j) {
       if (uv[j]) {
 #pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-          for (int b = 0; b < B; ++b)
-            acc[r * B + b] = unit_dot<FMT, XF16>(cur[r][j], xs[b][j], sh[j], acc[r * B + b]);
+        for (int r = 0; r < R; ++r) acc[r] = unit_dot<FMT, XF16>(cur[r][j], xs[j], sh[j], acc[r]);
       }
     }
 #pragma unroll
-    for (int i = 0; i < R * B; ++i) {
-      const float tot = group_sum<LPR>(acc[i], sub);
-      const int r = i / B, b = i % B;
-      const int row = grp * (R * RPW) + r * RPW + sub;
-      if (l == 0 && row < N) y[int64_t(b) * N + row] = tot;
+    for (int r = 0; r < R; ++r) {
+      const float tot = group_sum<LPR>(acc[r], sub);
+      const int row = (grp - sg.g0) * (R * RPW) + r * RPW + sub;
+      if (l == 0 && row < sg.N) sg.y[row] = tot;
     }
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -337,48 +364,54 @@ __global__ __launch_bounds__(kThreads) void matvec_xs_kernel(Geo g, const void* 
 }
 
 template <int FMT, bool XF16, int LPR, int UPL, int R>
-hipError_t go(const Geo& g, const void* x, float* y, int N, hipStream_t s) {
+hipError_t go(SegTable& t, hipStream_t s) {
   constexpr int rows_per_group = R * (64 / LPR);
-  const int ngroups = (N + rows_per_group - 1) / rows_per_group;
+  int g = 0;
+  for (int i = 0; i < t.count; ++i) {
+    t.s[i].g0 = g;
+    g += (t.s[i].N + rows_per_group - 1) / rows_per_group;
+  }
+  t.ngroups = g;
   // at most 16 waves per CU on 256 CUs; each wave then walks several groups
   const int max_blocks = 256 * 16 / kWaves;
-  int blocks = (ngroups + kWaves - 1) / kWaves;
+  int blocks = (t.ngroups + kWaves - 1) / kWaves;
   if (blocks > max_blocks) blocks = max_blocks;
-  hipLaunchKernelGGL((matvec_xs_kernel<FMT, XF16, LPR, UPL, R, 1>), dim3(blocks), dim3(kThreads), 0, s,
-                     g, x, y, N, ngroups);
+  hipLaunchKernelGGL((matvec_xs_kernel<FMT, XF16, LPR, UPL, R>), dim3(blocks), dim3(kThreads), 0, s, t);
   return hipGetLastError();
 }
 
 template <int FMT, bool XF16, int LPR, int UPL>
-hipError_t pick_r(const Geo& g, const void* x, float* y, int N, int rsel, hipStream_t s) {
-  const int groups_r1 = (N + (64 / LPR) - 1) / (64 / LPR);
+hipError_t pick_r(SegTable& t, int rsel, hipStream_t s) {
+  int64_t rows = 0;
+  for (int i = 0; i < t.count; ++i) rows += t.s[i].N;
+  const int64_t groups_r1 = rows / (64 / LPR);
   const int r = rsel ? rsel : (groups_r1 >= 4 * 4096 ? 2 : 1);
-  return r == 2 ? go<FMT, XF16, LPR, UPL, 2>(g, x, y, N, s) : go<FMT, XF16, LPR, UPL, 1>(g, x, y, N, s);
+  return r == 2 ? go<FMT, XF16, LPR, UPL, 2>(t, s) : go<FMT, XF16, LPR, UPL, 1>(t, s);
 }
 
 template <int FMT, bool XF16>
-bool dispatch(const Geo& g, const void* x, float* y, int N, int rsel, hipStream_t s, hipError_t* e) {
+bool dispatch(SegTable& t, int rsel, hipStream_t s, hipError_t* e) {
   constexpr bool H2 = (FMT == QMV_W4A16_G64 && XF16);
-  const int U = g.K / 32;
+  const int U = t.K / 32;
   const int lpr = U >= 64 ? 64 : (U > 16 ? 32 : 16);
   const int upl = (U + lpr - 1) / lpr;
   // activation registers per unit: 17 (fp16 pairs) or 34 (f32)
   if (upl > (H2 ? 4 : 3)) return false;
   if (lpr == 64) {
     switch (upl) {
-      case 1: *e = pick_r<FMT, XF16, 64, 1>(g, x, y, N, rsel, s); return true;
-      case 2: *e = pick_r<FMT, XF16, 64, 2>(g, x, y, N, rsel, s); return true;
-      case 3: *e = pick_r<FMT, XF16, 64, 3>(g, x, y, N, rsel, s); return true;
+      case 1: *e = pick_r<FMT, XF16, 64, 1>(t, rsel, s); return true;
+      case 2: *e = pick_r<FMT, XF16, 64, 2>(t, rsel, s); return true;
+      case 3: *e = pick_r<FMT, XF16, 64, 3>(t, rsel, s); return true;
       default:
-        if constexpr (H2) { *e = pick_r<FMT, XF16, 64, 4>(g, x, y, N, rsel, s); return true; }
+        if constexpr (H2) { *e = pick_r<FMT, XF16, 64, 4>(t, rsel, s); return true; }
         return false;
     }
   }
   if (lpr == 32) {
-    *e = upl == 1 ? pick_r<FMT, XF16, 32, 1>(g, x, y, N, rsel, s) : pick_r<FMT, XF16, 32, 2>(g, x, y, N, rsel, s);
+    *e = upl == 1 ? pick_r<FMT, XF16, 32, 1>(t, rsel, s) : pick_r<FMT, XF16, 32, 2>(t, rsel, s);
     return true;
   }
-  *e = pick_r<FMT, XF16, 16, 1>(g, x, y, N, rsel, s);
+  *e = pick_r<FMT, XF16, 16, 1>(t, rsel, s);
   return true;
 }
 
@@ -391,6 +424,19 @@ int rows_override() {
   return v;
 }
 
+bool launch_table(int fmt, SegTable& t, int x_dtype, hipStream_t s, hipError_t* err) {
+  const int rsel = rows_override();
+  const bool f16 = (x_dtype == QMV_F16);
+  switch (fmt) {
+    case QMV_Q8_0: return dispatch<QMV_Q8_0, false>(t, rsel, s, err);
+    case QMV_W4A16_G64:
+      return f16 ? dispatch<QMV_W4A16_G64, true>(t, rsel, s, err) : dispatch<QMV_W4A16_G64, false>(t, rsel, s, err);
+    case QMV_Q4K: return dispatch<QMV_Q4K, false>(t, rsel, s, err);
+    case QMV_Q6K: return dispatch<QMV_Q6K, false>(t, rsel, s, err);
+    default: return false;
+  }
+}
+
 }  // namespace
 
 // Single-vector matvec on the activation-stationary kernels.  Returns false
@@ -399,18 +445,40 @@ int rows_override() {
 bool launch_matvec_b1(int fmt, int64_t N, int64_t K, const uint8_t* W, const void* x, int x_dtype,
                       float* y, hipStream_t s, hipError_t* err) {
   const Planes p = planes_of(fmt, N, K);
-  const Geo g{W, p.off[1], p.off[2], p.off[3], int(K)};
-  const int rsel = rows_override();
-  const bool f16 = (x_dtype == QMV_F16);
-  switch (fmt) {
-    case QMV_Q8_0: return dispatch<QMV_Q8_0, false>(g, x, y, int(N), rsel, s, err);
-    case QMV_W4A16_G64:
-      return f16 ? dispatch<QMV_W4A16_G64, true>(g, x, y, int(N), rsel, s, err)
-                 : dispatch<QMV_W4A16_G64, false>(g, x, y, int(N), rsel, s, err);
-    case QMV_Q4K: return dispatch<QMV_Q4K, false>(g, x, y, int(N), rsel, s, err);
-    case QMV_Q6K: return dispatch<QMV_Q6K, false>(g, x, y, int(N), rsel, s, err);
-    default: return false;
+  SegTable t{};
+  t.count = 1;
+  t.K = int(K);
+  t.s[0] = Seg{W, p.off[1], p.off[2], p.off[3], x, y, int(N), 0};
+  return launch_table(fmt, t, x_dtype, s, err);
+}
+
+// Several single-vector matvecs of one format and one K in one launch per
+// kMaxSeg items.  Returns false (nothing launched) when the shape does not fit
+// the activation-stationary kernels.
+bool launch_matvec_grouped_b1(int fmt, int64_t K, int count, const qmv_matvec_item* items, int x_dtype,
+                              hipStream_t s, hipError_t* err) {
+  const int U = int(K) / 32;
+  const int lpr = U >= 64 ? 64 : (U > 16 ? 32 : 16);
+  const int upl = (U + lpr - 1) / lpr;
+  if (upl > ((fmt == QMV_W4A16_G64 && x_dtype == QMV_F16) ? 4 : 3)) return false;
+  // a launch takes up to kMaxSeg items and up to 2^30 rows (32-bit group indices)
+  const int64_t max_rows = int64_t(1) << 30;
+  for (int i0 = 0; i0 < count;) {
+    SegTable t{};
+    t.K = int(K);
+    int64_t rows = 0;
+    while (t.count < kMaxSeg && i0 + t.count < count && (t.count == 0 || rows + items[i0 + t.count].N <= max_rows)) {
+      const qmv_matvec_item& it = items[i0 + t.count];
+      const Planes p = planes_of(fmt, it.N, K);
+      t.s[t.count++] = Seg{static_cast<const uint8_t*>(it.W), p.off[1], p.off[2], p.off[3], it.x,
+                           static_cast<float*>(it.y), int(it.N), 0};
+      rows += it.N;
+    }
+    if (!launch_table(fmt, t, x_dtype, s, err)) return false;
+    if (*err != hipSuccess) return true;
+    i0 += t.count;
   }
+  return true;
 }
 
 }  // namespace qmv

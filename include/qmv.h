@@ -120,6 +120,14 @@ typedef struct qmv_logical {
   const void* aux[4];
 } qmv_logical;
 
+/* One matrix of a grouped matvec (all pointers are device pointers). */
+typedef struct qmv_matvec_item {
+  int64_t N;     /* rows of this matrix */
+  const void* W; /* packed matrix, layout above, 16-byte aligned */
+  const void* x; /* [batch][K] activations; items may share one x */
+  void* y;       /* [batch][N] output; must not overlap another item's y */
+} qmv_matvec_item;
+
 /* ABI version (QMV_ABI_VERSION); *layout_version receives QMV_LAYOUT_VERSION if non-NULL. */
 int qmv_abi_version(int* layout_version);
 
@@ -159,6 +167,22 @@ int qmv_pack(int fmt, int64_t N, int64_t K, int64_t batch, const qmv_logical* sr
  */
 int qmv_matvec(int fmt, int64_t N, int64_t K, int64_t batch, const void* W,
                const void* x, int x_dtype, void* y, int y_dtype, void* stream);
+
+/*
+ * Several matvecs of one format, one K and one batch in as few launches as
+ * possible: for every item i, y_i[b][n] = sum_k W_i[n][k] * x_i[b][k].
+ * The grouped dispatch of the pages' decoders: the q / k / v projections in
+ * one dispatch with the simdgroups spread over the three matrices, gate / up
+ * in another (aot-llm README, Metal backend notes).  At batch 1, up to 16
+ * items share one launch (their row groups are laid end to end and each wave
+ * reloads x only when it moves to an item with other activations); other
+ * batches run one qmv_matvec launch per item.  Dtypes and alignment as
+ * qmv_matvec; count >= 1.
+ * Errors: FORMAT, SHAPE, NULL, ALIGN, DTYPE, UNSUPPORTED, OVERFLOW, DEVICE, LAUNCH
+ * (the message names the offending item).
+ */
+int qmv_matvec_grouped(int fmt, int64_t K, int64_t batch, int count, const qmv_matvec_item* items,
+                       int x_dtype, int y_dtype, void* stream);
 
 /*
  * Y[m][n] = sum_k X[m][k] * W[n][k] for m < M, on bf16 matrix cores with f32

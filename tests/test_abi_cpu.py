@@ -30,7 +30,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
         ["qmv_abi_version", "qmv_status_string", "qmv_last_error", "qmv_packed_bytes",
-         "qmv_pack", "qmv_matvec", "qmv_gemm", "qmv_dequant"])
+         "qmv_pack", "qmv_matvec", "qmv_matvec_grouped", "qmv_gemm", "qmv_dequant"])
 
 
 def test_library_exports_every_declared_symbol(q):
@@ -103,3 +103,23 @@ def test_gemm_and_pack_argument_errors(q):
     assert q.raw_call("qmv_pack", 3, 8, 256, 1, None, P, None) == -1
     assert q.raw_call("qmv_pack", 3, 8, 256, 1, ctypes.byref(src), P + 8, None) == -5
     assert q.raw_call("qmv_dequant", 4, 8, 256, P, P + 4, None) == -5
+
+
+def test_grouped_argument_errors(q):
+    P = 1 << 20
+    items = (q.QmvMatvecItem * 2)()
+    for it in items:
+        it.N, it.W, it.x, it.y = 64, P, P, P
+    call = lambda *a: q.raw_call("qmv_matvec_grouped", *a)  # noqa: E731
+    assert call(3, 256, 1, 0, items, 1, 1, None) == -4
+    assert call(3, 256, 1, 2, None, 1, 1, None) == -1
+    items[1].W = None
+    assert call(3, 256, 1, 2, items, 1, 1, None) == -1
+    assert "items[1].W" in q.last_error()
+    items[1].W = P + 8
+    assert call(3, 256, 1, 2, items, 1, 1, None) == -5
+    items[1].W, items[1].N = P, 0
+    assert call(3, 256, 1, 2, items, 1, 1, None) == -4
+    items[1].N = 64
+    assert call(3, 200, 1, 2, items, 1, 1, None) == -4
+    assert call(3, 256, 1, 2, items, 2, 1, None) == -3

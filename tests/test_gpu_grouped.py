@@ -1,0 +1,175 @@
+"""GPU parity of the grouped matvec (several matrices of one format and K per
+call) against the CPU oracle, and against one qmv_matvec call per matrix.
+
+Bar: every output within 1e-3 * ||W_row|| * ||x|| of the f64 oracle; with
+the same inputs the grouped call returns exactly what the single calls
+return (each row is summed in the same order whichever matrix it belongs to).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from gpu_helpers import TAU, dev_x, pack_dev, x_values
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _make(qmv, fmt, shapes, K, batch, x_dtype, shared_x, seed):
+    """Seeded matrices of the given row counts, packed, plus their activations."""
+    ws, Wps, xs = [], [], []
+    x0 = wl.gen_x(K, batch, x_dtype, (30, seed, 0))
+    for i, N in enumerate(shapes):
+        w = wl.gen_weights(fmt, N, K, (30, seed, i + 1))
+        ws.append(w)
+        Wps.append(pack_dev(qmv, fmt, w))
+        xs.append(x0 if shared_x else wl.gen_x(K, batch, x_dtype, (30, seed, 100 + i)))
+    return ws, Wps, xs
+
+
+def _run_and_check(qmv, fmt, shapes, K, batch, x_dtype, shared_x, seed, rows_cap=None):
+    ws, Wps, xs = _make(qmv, fmt, shapes, K, batch, x_dtype, shared_x, seed)
+    xd = {}
+    items = []
+    for i, (Wp, x) in enumerate(zip(Wps, xs)):
+        key = id(x)
+        if key not in xd:
+            xd[key] = dev_x(x, x_dtype)
+        items.append((Wp, xd[key], shapes[i]))
+    ys = qmv.matvec_grouped(fmt, items, K)
+    torch.cuda.synchronize()
+    for i, (w, x, y) in enumerate(zip(ws, xs, ys)):
+        N = shapes[i]
+        rows = np.arange(N)
+        if rows_cap is not None and N > rows_cap:
+            g = np.random.default_rng(i)
+            rows = np.unique(np.concatenate([[0, N - 1], g.integers(0, N, rows_cap)]))
+        W32 = oracle.dequant_rows(fmt, w, rows)
+        xv = x_values(x, x_dtype)
+        ref = oracle.matvec_ref(W32, xv)
+        bound = oracle.tolerance_bound(W32, xv, TAU["matvec"])
+        r = oracle.check_within(y.cpu().numpy()[:, rows], ref, bound)
+        assert r["ok"], (fmt, i, N, r)
+    return ws, Wps, xd, items, ys
+
+
+XDT = {"q8_0": "f32", "w4a16_g64": "f16", "q4k": "f32", "q6k": "f32"}
+
+
+@pytest.mark.parametrize("fmt", wl.FORMATS)
+@pytest.mark.parametrize("shared_x", [True, False])
+def test_grouped_parity_ragged(qmv, fmt, shared_x):
+    K = wl.BLOCK[fmt] * 8
+    shapes = [1, 67, 300, 5, 129]
+    _say(fmt, shared_x, shapes, K)
+    _run_and_check(qmv, fmt, shapes, K, 1, XDT[fmt], shared_x, seed=1)
+
+
+def test_grouped_w4a16_f32_activations(qmv):
+    _run_and_check(qmv, "w4a16_g64", [640, 64, 3], 2048, 1, "f32", False, seed=2)
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "w4a16_g64"])
+def test_grouped_more_items_than_one_launch_holds(qmv, fmt):
+    # 37 items: three launches of up to 16; x shared in runs of three
+    K = wl.BLOCK[fmt] * 4
+    shapes = [int(n) for n in np.random.default_rng(3).integers(1, 200, 37)]
+    ws, Wps, xs = _make(qmv, fmt, shapes, K, 1, XDT[fmt], False, seed=3)
+    xdev = [dev_x(xs[i - i % 3], XDT[fmt]) for i in range(len(shapes))]
+    ys = qmv.matvec_grouped(fmt, [(Wps[i], xdev[i], shapes[i]) for i in range(len(shapes))], K)
+    torch.cuda.synchronize()
+    for i in range(len(shapes)):
+        W32 = oracle.dequant_rows(fmt, ws[i], np.arange(shapes[i]))
+        xv = x_values(xs[i - i % 3], XDT[fmt])
+        r = oracle.check_within(ys[i].cpu().numpy(), oracle.matvec_ref(W32, xv),
+                                oracle.tolerance_bound(W32, xv, TAU["matvec"]))
+        assert r["ok"], (i, r)
+
+
+@pytest.mark.parametrize("fmt", wl.FORMATS)
+def test_grouped_equals_single_calls_bitwise(qmv, fmt):
+    K = wl.BLOCK[fmt] * 16
+    shapes = [700, 64, 2049]
+    ws, Wps, xd, items, ys = _run_and_check(qmv, fmt, shapes, K, 1, XDT[fmt], True, seed=4)
+    for (Wp, x, N), y in zip(items, ys):
+        single = qmv.matvec(fmt, Wp, x, N, K)
+        torch.cuda.synchronize()
+        assert torch.equal(single.view(torch.int32), y.view(torch.int32))
+
+
+@pytest.mark.parametrize("batch", [2, 8])
+def test_grouped_batched_runs_per_item(qmv, batch):
+    _run_and_check(qmv, "q4k", [300, 17], 1024, batch, "f32", True, seed=5)
+
+
+def test_grouped_wide_k_falls_back(qmv):
+    # K = 16384 with f32 activations needs more activation registers than the
+    # grouped single-vector kernel holds: one launch per item instead
+    _run_and_check(qmv, "q8_0", [40, 9], 16384, 1, "f32", False, seed=6)
+
+
+def test_grouped_graph_replay(qmv):
+    fmt, K = "q4k", 2048
+    shapes = [2048, 256, 5632]
+    ws, Wps, xs = _make(qmv, fmt, shapes, K, 1, "f32", True, seed=7)
+    x = dev_x(xs[0], "f32")
+    items = [(Wps[i], x, shapes[i]) for i in range(3)]
+    eager = [y.clone() for y in qmv.matvec_grouped(fmt, items, K)]
+    outs = [torch.empty_like(e) for e in eager]
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        qmv.matvec_grouped(fmt, [it + (o,) for it, o in zip(items, outs)], K)
+    for _ in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o, e)
+
+
+def test_config_w4a16_gate_up_grouped(qmv):
+    # the 1.1B MLP's gate and up projections share x: one grouped call
+    c = wl.c2_w4a16_mlp()
+    (_, fmt, N, K, kg), (_, _, _, _, ku) = c["mats"][0], c["mats"][1]
+    wg, wu = wl.gen_weights(fmt, N, K, kg), wl.gen_weights(fmt, N, K, ku)
+    x = wl.gen_x(K, 1, "f16", kg)
+    xt = dev_x(x, "f16")
+    yg, yu = qmv.matvec_grouped(fmt, [(pack_dev(qmv, fmt, wg), xt, N), (pack_dev(qmv, fmt, wu), xt, N)], K)
+    torch.cuda.synchronize()
+    xv = x_values(x, "f16")
+    for w, y in ((wg, yg), (wu, yu)):
+        W32 = oracle.dequant_rows(fmt, w, np.arange(N))
+        r = oracle.check_within(y.cpu().numpy(), oracle.matvec_ref(W32, xv),
+                                oracle.tolerance_bound(W32, xv, TAU["matvec"]))
+        _say(r)
+        assert r["ok"], r
+
+
+def test_config_decode_layer_qkv_grouped(qmv):
+    # q and k (Q4K) of one 1.1B decoder layer in one call, v (Q6K) in another
+    layer = [m for m in wl.c5_sweep(1, layers=1)["mats"] if m[0] in ("l0.q", "l0.k", "l0.v")]
+    x = wl.gen_x(2048, 1, "f32", (31, 0, 0))
+    xt = dev_x(x, "f32")
+    xv = x_values(x, "f32")
+    ws = {nm: wl.gen_weights(fmt, N, K, key) for nm, fmt, N, K, key in layer}
+    fmts = {nm: (fmt, N) for nm, fmt, N, K, key in layer}
+    yq, yk = qmv.matvec_grouped("q4k", [(pack_dev(qmv, "q4k", ws[n]), xt, fmts[n][1]) for n in ("l0.q", "l0.k")],
+                                2048)
+    (yv,) = qmv.matvec_grouped("q6k", [(pack_dev(qmv, "q6k", ws["l0.v"]), xt, 256)], 2048)
+    torch.cuda.synchronize()
+    for nm, y in (("l0.q", yq), ("l0.k", yk), ("l0.v", yv)):
+        fmt, N = fmts[nm]
+        W32 = oracle.dequant_rows(fmt, ws[nm], np.arange(N))
+        r = oracle.check_within(y.cpu().numpy(), oracle.matvec_ref(W32, xv),
+                                oracle.tolerance_bound(W32, xv, TAU["matvec"]))
+        _say(nm, r)
+        assert r["ok"], (nm, r)
