@@ -6,8 +6,9 @@ of algorithmic bytes, on the group-64 W4A16 MLP matvecs of a 1.1B-parameter
 decoder (gate / up 5632 x 2048, down 2048 x 5632, batch 1, fp16 activations).
 A step is one decode token's MLP matvecs over `--copies` distinct weight sets
 (default 32, 623 MB), so every step streams its weights from HBM rather than
-from the 256 MB Infinity Cache; the 3 x copies launches are captured once in a
-HIP graph and replayed.  Inputs are resident in HBM before timing starts.
+from the 256 MB Infinity Cache.  Per weight set, gate and up read the same
+activations and run as one grouped launch, down as a second; the 2 x copies
+launches are captured once in a HIP graph and replayed.  Inputs are resident in HBM before timing starts.
 
 Algorithmic bytes of one matvec = packed weights including scales / zeros
 (4.5 bits per weight) + activations read + outputs written; the dense
@@ -139,42 +140,98 @@ class Stream:
 
 # ------------------------------------------------------------------ legs
 
+class MlpStream:
+    """One decode token's MLP matvecs over `copies` distinct weight sets (each a
+    layer's gate / up / down, packed once and cloned): per layer, gate and up
+    read the same activations and run as one grouped launch, down as another."""
+
+    def __init__(self, qmv, cfg, copies):
+        import torch
+        import workloads as wl
+        self.qmv, self.x_dtype, self.mats = qmv, cfg["x_dtype"], cfg["mats"]
+        (_, fmt, F, D, kg), (_, _, _, _, ku), (_, _, _, _, kd) = cfg["mats"]
+        self.fmt, self.F, self.D = fmt, F, D
+        self.logical = {}
+        packed = {}
+        for name, f, N, K, key in cfg["mats"]:
+            w = wl.gen_weights(f, N, K, key)
+            self.logical[name] = (f, w, wl.gen_x(K, 1, self.x_dtype, key))
+            packed[name] = qmv.pack(f, {k: _dev(v) for k, v in w.items()})
+        self.layers = []
+        for c in range(copies):
+            W = {n: packed[n] if c == 0 else packed[n].clone() for n in packed}
+            xi = _x_dev(wl.gen_x(D, 1, self.x_dtype, (kg[0], kg[1], kg[2], 77, c)), self.x_dtype)
+            xm = _x_dev(wl.gen_x(F, 1, self.x_dtype, (kd[0], kd[1], kd[2], 77, c)), self.x_dtype)
+            ys = [torch.empty((1, n), dtype=torch.float32, device="cuda") for n in (F, F, D)]
+            self.layers.append((W["gate"], W["up"], W["down"], xi, xm, ys))
+        xb = 2 if self.x_dtype == "f16" else 4
+        self.gate_up_bytes = gate_up_bytes(fmt, F, D, xb)
+        self.down_bytes = matvec_bytes(fmt, D, F, 1, xb)
+        self.bytes = copies * (self.gate_up_bytes + self.down_bytes)
+        self.launches = 2 * copies
+
+    def gate_up(self, layer):
+        Wg, Wu, _, xi, _, (yg, yu, _) = layer
+        self.qmv.matvec_grouped(self.fmt, [(Wg, xi, self.F, yg), (Wu, xi, self.F, yu)], self.D)
+
+    def down(self, layer):
+        _, _, Wd, _, xm, (_, _, yd) = layer
+        self.qmv.matvec(self.fmt, Wd, xm, self.D, self.F, y=yd)
+
+    def __call__(self):
+        for layer in self.layers:
+            self.gate_up(layer)
+            self.down(layer)
+
+    def ungrouped(self):
+        """The same work as three single matvecs per layer (for comparison)."""
+        mv = self.qmv.matvec
+        for Wg, Wu, Wd, xi, xm, (yg, yu, yd) in self.layers:
+            mv(self.fmt, Wg, xi, self.F, self.D, y=yg)
+            mv(self.fmt, Wu, xi, self.F, self.D, y=yu)
+            mv(self.fmt, Wd, xm, self.D, self.F, y=yd)
+
+
+def gate_up_bytes(fmt, F, D, xb):
+    """Algorithmic bytes of the grouped gate + up launch: both matrices, the
+    shared activations once, both outputs."""
+    import workloads as wl
+    return 2 * int(round(wl.bytes_per_weight(fmt) * F * D)) + D * xb + 2 * F * 4
+
+
 def headline(qmv, args):
     import workloads as wl
-    c2 = wl.c2_w4a16_mlp()
-    st = Stream(qmv, c2["mats"], c2["x_dtype"], 1, args.copies)
+    st = MlpStream(qmv, wl.c2_w4a16_mlp(), args.copies)
     ms, _ = time_graph(st, args.steps, args.warmup)
     gbs = st.bytes / (ms * 1e-3) / 1e9
     return st, ms, gbs
 
 
 def kernel_leg(qmv, st, steps, warmup):
-    """Per-launch duration of each matvec shape of the headline stream: a graph of
-    back-to-back launches of that shape over all its cold copies, timed with events."""
+    """Per-launch duration of each launch of the headline step: a graph of the
+    launches of one kind over all cold copies, back to back, timed with events
+    on the stream they run on."""
     out = {}
-    for name, fmt, N, K, key in st.mats:
-        items = [it for it in st.items if (it[1], it[2]) == (N, K)]
-        # shapes shared by two names (gate/up) are timed once
-        tag = f"{fmt} {N}x{K}"
-        if tag in out:
-            continue
-
-        def run(items=items):
-            for f, n, k, W, x, y in items:
-                qmv.matvec(f, W, x, n, k, y=y)
+    for tag, fn, b in (("gate+up grouped", st.gate_up, st.gate_up_bytes), ("down", st.down, st.down_bytes)):
+        def run(fn=fn):
+            for layer in st.layers:
+                fn(layer)
         ms, _ = time_graph(run, steps, warmup)
-        per = ms / len(items)
-        b = matvec_bytes(fmt, N, K, 1, 2)
+        per = ms / len(st.layers)
         out[tag] = {"us_per_launch": per * 1e3, "bytes_per_launch": b,
-                    "gbs": b / (per * 1e-3) / 1e9, "launches": len(items)}
+                    "gbs": b / (per * 1e-3) / 1e9, "launches": len(st.layers)}
+    ms, _ = time_graph(st.ungrouped, steps, warmup)
+    out["step_ungrouped"] = {"ms_per_step": ms, "gbs": st.bytes / (ms * 1e-3) / 1e9,
+                             "launches": 3 * len(st.layers)}
     return out
 
 
 # Source files of the matvec kernels the headline launches, and the kernel
-# instantiation the dispatcher picks for the gate / up shape (fp16 x, K = 2048:
-# 64 lanes per row, one unit per lane, one row per lane group, one vector).
+# instantiation the dispatcher picks for the grouped gate / up launch (fp16 x,
+# K = 2048: 64 lanes per row, one unit per lane, two rows per lane group, two
+# segments).
 MATVEC_SOURCES = ["gemm_dequant_matvec_amd/csrc/matvec_xs.hip", "gemm_dequant_matvec_amd/csrc/qmv_internal.h"]
-GATE_KERNEL = "matvec_xs_kernel<2, true, 64, 1, 1, 1>"
+GATE_KERNEL = "matvec_xs_kernel<2, true, 64, 1, 2, false>"
 
 
 def measured_traffic(profile: str, kernel: str):
@@ -244,7 +301,8 @@ def extras(qmv, args):
         ms, _ = time_graph(st, 10, 3)
         res[f"decode_sweep_1.1B_b{b}"] = {
             "ms_per_token_step": ms, "tok_per_s": b / (ms * 1e-3),
-            "gbs": st.bytes / (ms * 1e-3) / 1e9, "bytes": st.bytes, "launches": st.launches}
+            "gbs": st.bytes / (ms * 1e-3) / 1e9, "bytes": st.bytes, "launches": st.launches,
+            "matvecs": st.matvecs}
         del st
     # prefill GEMM
     for M in (16, 128, 512):
@@ -255,27 +313,52 @@ def extras(qmv, args):
     return res
 
 
-class Sweep(Stream):
+class Sweep:
     """The 155 matvecs of one decode token: distinct shapes generated once, every
-    layer gets its own device copy (so the 667 MB sweep streams from HBM)."""
+    layer gets its own device copy (so the 667 MB sweep streams from HBM).
+    Matrices that read the same activations and share a format run as one
+    grouped call: q + k (Q4K), gate + up; v (Q6K), o, down and the head alone."""
+
+    SHARED = {"q": "attn_in", "k": "attn_in", "v": "attn_in", "gate": "mlp_in", "up": "mlp_in"}
 
     def __init__(self, qmv, cfg, batch):
+        import torch
         import workloads as wl
         self.qmv, self.batch = qmv, batch
-        shapes = {}
-        self.items = []
+        shapes, xs = {}, {}
+        self.calls = []  # (fmt, K, [(W, x, N, y), ...])
+        prev = None
+        self.bytes = 0
         for name, fmt, N, K, key in cfg["mats"]:
             tag = (fmt, N, K)
             if tag not in shapes:
                 w = wl.gen_weights(fmt, N, K, key)
-                shapes[tag] = qmv.pack(fmt, {k: _dev(v) for k, v in w.items()})
-                W = shapes[tag]
+                shapes[tag] = W = qmv.pack(fmt, {k: _dev(v) for k, v in w.items()})
             else:
                 W = shapes[tag].clone()
-            x = _x_dev(wl.gen_x(K, batch, "f32", key), "f32")
-            self.items.append((fmt, N, K, W, x, self._out(N)))
-        self.bytes = sum(matvec_bytes(f, N, K, batch, 4) for f, N, K, *_ in self.items)
-        self.launches = len(self.items)
+            layer, nm = name.split(".") if "." in name else ("", name)
+            share = (layer, self.SHARED.get(nm, nm))
+            if share not in xs:
+                xs[share] = _x_dev(wl.gen_x(K, batch, "f32", key), "f32")
+                self.bytes += batch * K * 4
+            y = torch.empty((batch, N), dtype=torch.float32, device="cuda")
+            self.bytes += int(round(wl.bytes_per_weight(fmt) * N * K)) + batch * N * 4
+            item = (W, xs[share], N, y)
+            if prev == (share, fmt, K):
+                self.calls[-1][2].append(item)
+            else:
+                self.calls.append((fmt, K, [item]))
+            prev = (share, fmt, K)
+        self.launches = len(self.calls) if batch == 1 else sum(len(c[2]) for c in self.calls)
+        self.matvecs = sum(len(c[2]) for c in self.calls)
+
+    def __call__(self):
+        for fmt, K, items in self.calls:
+            if len(items) == 1:
+                W, x, N, y = items[0]
+                self.qmv.matvec(fmt, W, x, N, K, y=y)
+            else:
+                self.qmv.matvec_grouped(fmt, items, K)
 
 
 def gemm_leg(qmv, M, reps=20):
@@ -355,21 +438,21 @@ def main():
     log(f"  {ms * 1e3:.1f} us/step, {gbs:.1f} GB/s")
     kl = kernel_leg(qmv, st, 20, 5)
     log("  per-shape:", json.dumps(kl))
-    # the gate / up shape: two of every three launches and most of the step's time
-    dom_tag = "w4a16_g64 5632x2048"
+    # the grouped gate / up launch: two thirds of the step's bytes and time
+    dom_tag = "gate+up grouped"
     dom = kl[dom_tag]
     traffic = measured_traffic("matvec_w4a16_g64_1.1B_mlp_b1", GATE_KERNEL)
     roofline = {"bound": "hbm", "achieved": dom["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": dom["gbs"] / HBM_PEAK_GBS, "traffic": traffic,
-                "kernel": f"{GATE_KERNEL} ({dom_tag})",
+                "kernel": f"{GATE_KERNEL} (gate+up grouped, 2 x 5632x2048)",
                 "us_per_launch": dom["us_per_launch"], "bytes_per_launch": dom["bytes_per_launch"]}
     out = {
         "metric": "decode matvec achieved HBM GB/s (% of peak); prefill GEMM TFLOP/s",
         "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f16*f16->f32", "data": "synthetic (seeded random blocks and activations, 1.1B-decoder shapes)",
-        "config": {"workload": "W4A16-g64 decode matvec, 1.1B-decoder MLP (gate, up 5632x2048; "
-                               "down 2048x5632), batch 1, fp16 x",
+        "config": {"workload": "W4A16-g64 decode matvec, 1.1B-decoder MLP (gate, up 5632x2048 "
+                               "as one grouped launch; down 2048x5632), batch 1, fp16 x",
                    "copies": args.copies, "launches_per_step": st.launches,
                    "bytes_per_step": st.bytes, "frac_of_peak": gbs / HBM_PEAK_GBS},
         "roofline": roofline,

@@ -13,6 +13,7 @@
 //    flight and the first loads leave before anything else happens.
 //  * Partial sums are reduced across the LPR lanes of a row with DPP moves
 //    inside 16-lane rows and ds_bpermute only across rows.
+#include <algorithm>
 #include <cstdlib>
 
 #include "qmv_internal.h"
@@ -264,8 +265,10 @@ __device__ __forceinline__ float unit_dot(const Raw<FMT>& w, const XUnit<FMT == 
 
 // Up to kMaxSeg matrices of one format and one K per launch.  Each segment is
 // one matvec (its packed planes, x, y, row count) and owns a contiguous range
-// of row groups; the table travels in the kernel arguments (no device copy,
-// so launches stay graph-capturable).
+// of blocks, sized in proportion to its rows; a block finds its segment once,
+// at start, and its waves then stride over that segment's row groups only.
+// The table travels in the kernel arguments (no device copy, so launches stay
+// graph-capturable).
 constexpr int kMaxSeg = 16;
 struct Seg {
   const uint8_t* W;
@@ -273,28 +276,40 @@ struct Seg {
   const void* x;
   float* y;
   int N;
-  int g0;  // first row group of this segment
+  int b0;  // first block of this segment
+  int nb;  // blocks of this segment
 };
 struct SegTable {
   Seg s[kMaxSeg];
   int count;
-  int ngroups;  // total row groups
   int K;
 };
 
 // FMT / XF16: format and activation type; LPR lanes per row; UPL units per lane
-// (covers K = 32 * LPR * UPL, ragged tail masked); R rows per lane group.
-template <int FMT, bool XF16, int LPR, int UPL, int R>
+// (covers K = 32 * LPR * UPL, ragged tail masked); R rows per lane group; ONE:
+// the table holds one segment (its fields then load at fixed offsets, with no
+// scan in front of them).
+template <int FMT, bool XF16, int LPR, int UPL, int R, bool ONE>
 __global__ __launch_bounds__(kThreads) void matvec_xs_kernel(const SegTable t) {
   constexpr bool H2 = (FMT == QMV_W4A16_G64 && XF16);
   constexpr int RPW = 64 / LPR;
   const int lane = threadIdx.x & 63;
   const int sub = lane / LPR;
   const int l = lane % LPR;
-  const int gw = blockIdx.x * kWaves + (threadIdx.x >> 6);
-  const int TW = gridDim.x * kWaves;
   const int K = t.K;
   const int U = K >> 5;
+
+  // this block's segment (block-uniform scan of at most kMaxSeg entries)
+  int si = 0;
+  if constexpr (!ONE)
+    for (int i = 1; i < t.count; ++i) si = (int(blockIdx.x) >= t.s[i].b0) ? i : si;
+  const Seg& sg = t.s[si];
+  const Geo g{sg.W, sg.off1, sg.off2, sg.off3, K};
+  const int N = sg.N;
+  float* __restrict__ y = sg.y;
+  const int ngroups = (N + R * RPW - 1) / (R * RPW);
+  const int gw = (int(blockIdx.x) - sg.b0) * kWaves + (threadIdx.x >> 6);
+  const int TW = sg.nb * kWaves;
 
   int uu[UPL], sh[UPL];
   bool uv[UPL];
@@ -306,40 +321,26 @@ __global__ __launch_bounds__(kThreads) void matvec_xs_kernel(const SegTable t) {
     sh[j] = 6 * (uu[j] & 7);
   }
 
-  // segment holding row group gi (wave-uniform scan of at most kMaxSeg entries)
-  auto seg_of = [&](int gi) {
-    int si = 0;
-    for (int i = 1; i < t.count; ++i) si = (gi >= t.s[i].g0) ? i : si;
-    return si;
-  };
+  int grp = gw;
+  Raw<FMT> cur[R][UPL];
   auto load_group = [&](Raw<FMT> (&dst)[R][UPL], int gi) {
-    const Seg& sg = t.s[seg_of(gi)];
-    const Geo geo{sg.W, sg.off1, sg.off2, sg.off3, K};
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int row = min((gi - sg.g0) * (R * RPW) + r * RPW + sub, sg.N - 1);
+      const int row = min(gi * (R * RPW) + r * RPW + sub, N - 1);
 #pragma unroll
-      for (int j = 0; j < UPL; ++j) dst[r][j] = load_raw<FMT>(geo, row, uu[j]);
+      for (int j = 0; j < UPL; ++j) dst[r][j] = load_raw<FMT>(g, row, uu[j]);
     }
   };
-
-  int grp = gw;
-  if (grp >= t.ngroups) return;  // the whole wave leaves; no block-level barrier follows
-  Raw<FMT> cur[R][UPL];
-  load_group(cur, grp);
+  if (grp < ngroups) load_group(cur, grp);
 
   XUnit<H2> xs[UPL];
-  const void* xcur = nullptr;
-  for (; grp < t.ngroups; grp += TW) {
+#pragma unroll
+  for (int j = 0; j < UPL; ++j) load_x<FMT, XF16>(xs[j], sg.x, 32 * uu[j], uv[j]);
+
+  for (; grp < ngroups; grp += TW) {
     Raw<FMT> nxt[R][UPL];
     const int gn = grp + TW;
-    if (gn < t.ngroups) load_group(nxt, gn);
-    const Seg& sg = t.s[seg_of(grp)];
-    if (sg.x != xcur) {  // a segment with other activations: reload this lane's slice
-      xcur = sg.x;
-#pragma unroll
-      for (int j = 0; j < UPL; ++j) load_x<FMT, XF16>(xs[j], xcur, 32 * uu[j], uv[j]);
-    }
+    if (gn < ngroups) load_group(nxt, gn);
     float acc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = 0.0f;
@@ -353,8 +354,8 @@ __global__ __launch_bounds__(kThreads) void matvec_xs_kernel(const SegTable t) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const float tot = group_sum<LPR>(acc[r], sub);
-      const int row = (grp - sg.g0) * (R * RPW) + r * RPW + sub;
-      if (l == 0 && row < sg.N) sg.y[row] = tot;
+      const int row = grp * (R * RPW) + r * RPW + sub;
+      if (l == 0 && row < N) y[row] = tot;
     }
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -363,29 +364,48 @@ __global__ __launch_bounds__(kThreads) void matvec_xs_kernel(const SegTable t) {
   }
 }
 
+// Blocks per segment: the whole launch is capped at 16 waves per CU on 256
+// CUs (each wave then walks several row groups); each segment gets a share
+// in proportion to its row groups, at least one block and no more blocks
+// than it has groups to hand out.
 template <int FMT, bool XF16, int LPR, int UPL, int R>
 hipError_t go(SegTable& t, hipStream_t s) {
   constexpr int rows_per_group = R * (64 / LPR);
-  int g = 0;
+  const int64_t max_blocks = 256 * 16 / kWaves;
+  int64_t groups[kMaxSeg], total = 0;
   for (int i = 0; i < t.count; ++i) {
-    t.s[i].g0 = g;
-    g += (t.s[i].N + rows_per_group - 1) / rows_per_group;
+    groups[i] = (t.s[i].N + rows_per_group - 1) / rows_per_group;
+    total += groups[i];
   }
-  t.ngroups = g;
-  // at most 16 waves per CU on 256 CUs; each wave then walks several groups
-  const int max_blocks = 256 * 16 / kWaves;
-  int blocks = (t.ngroups + kWaves - 1) / kWaves;
-  if (blocks > max_blocks) blocks = max_blocks;
-  hipLaunchKernelGGL((matvec_xs_kernel<FMT, XF16, LPR, UPL, R>), dim3(blocks), dim3(kThreads), 0, s, t);
+  const int64_t budget = std::min<int64_t>((total + kWaves - 1) / kWaves, max_blocks);
+  int b = 0;
+  for (int i = 0; i < t.count; ++i) {
+    const int64_t need = (groups[i] + kWaves - 1) / kWaves;
+    const int64_t share = (budget * groups[i] + total - 1) / total;
+    t.s[i].b0 = b;
+    t.s[i].nb = int(std::max<int64_t>(1, std::min(need, share)));
+    b += t.s[i].nb;
+  }
+  if (t.count == 1)
+    hipLaunchKernelGGL((matvec_xs_kernel<FMT, XF16, LPR, UPL, R, true>), dim3(b), dim3(kThreads), 0, s, t);
+  else
+    hipLaunchKernelGGL((matvec_xs_kernel<FMT, XF16, LPR, UPL, R, false>), dim3(b), dim3(kThreads), 0, s, t);
   return hipGetLastError();
 }
 
+// Rows per lane group, from measurements on MI355X (W4A16 / Q4K / Q6K, K = 1024
+// to 5632): two rows once a launch streams 2 MB or more (twice the loads in
+// flight per wave and half the activation reloads outweigh the waves lost),
+// four once every wave slot of the chip (4096) would walk 16 rows or more,
+// one row below 2 MB, where the launch is latency-bound and waves count.
 template <int FMT, bool XF16, int LPR, int UPL>
 hipError_t pick_r(SegTable& t, int rsel, hipStream_t s) {
   int64_t rows = 0;
   for (int i = 0; i < t.count; ++i) rows += t.s[i].N;
-  const int64_t groups_r1 = rows / (64 / LPR);
-  const int r = rsel ? rsel : (groups_r1 >= 4 * 4096 ? 2 : 1);
+  const int64_t weight_bytes = rows * int64_t(t.K) * (FMT == QMV_Q8_0 ? 34 : FMT == QMV_Q6K ? 26 : 18) / 32;
+  const int64_t rows_per_slot = rows / (64 / LPR) / 4096;
+  const int r = rsel ? rsel : rows_per_slot >= 16 ? 4 : weight_bytes >= (int64_t(2) << 20) ? 2 : 1;
+  if (r == 4) return go<FMT, XF16, LPR, UPL, 4>(t, s);
   return r == 2 ? go<FMT, XF16, LPR, UPL, 2>(t, s) : go<FMT, XF16, LPR, UPL, 1>(t, s);
 }
 
@@ -417,9 +437,9 @@ bool dispatch(SegTable& t, int rsel, hipStream_t s, hipError_t* e) {
 
 int rows_override() {
   static const int v = [] {
-    const char* e = getenv("QMV_MATVEC_ROWS");  // A/B tuning only: rows per lane group (1 or 2)
+    const char* e = getenv("QMV_MATVEC_ROWS");  // A/B tuning only: rows per lane group (1, 2 or 4)
     const int r = e ? atoi(e) : 0;
-    return (r == 1 || r == 2) ? r : 0;
+    return (r == 1 || r == 2 || r == 4) ? r : 0;
   }();
   return v;
 }
@@ -448,7 +468,7 @@ bool launch_matvec_b1(int fmt, int64_t N, int64_t K, const uint8_t* W, const voi
   SegTable t{};
   t.count = 1;
   t.K = int(K);
-  t.s[0] = Seg{W, p.off[1], p.off[2], p.off[3], x, y, int(N), 0};
+  t.s[0] = Seg{W, p.off[1], p.off[2], p.off[3], x, y, int(N), 0, 0};
   return launch_table(fmt, t, x_dtype, s, err);
 }
 
@@ -461,7 +481,7 @@ bool launch_matvec_grouped_b1(int fmt, int64_t K, int count, const qmv_matvec_it
   const int lpr = U >= 64 ? 64 : (U > 16 ? 32 : 16);
   const int upl = (U + lpr - 1) / lpr;
   if (upl > ((fmt == QMV_W4A16_G64 && x_dtype == QMV_F16) ? 4 : 3)) return false;
-  // a launch takes up to kMaxSeg items and up to 2^30 rows (32-bit group indices)
+  // a launch takes up to kMaxSeg items and up to 2^30 rows
   const int64_t max_rows = int64_t(1) << 30;
   for (int i0 = 0; i0 < count;) {
     SegTable t{};
@@ -471,7 +491,7 @@ bool launch_matvec_grouped_b1(int fmt, int64_t K, int count, const qmv_matvec_it
       const qmv_matvec_item& it = items[i0 + t.count];
       const Planes p = planes_of(fmt, it.N, K);
       t.s[t.count++] = Seg{static_cast<const uint8_t*>(it.W), p.off[1], p.off[2], p.off[3], it.x,
-                           static_cast<float*>(it.y), int(it.N), 0};
+                           static_cast<float*>(it.y), int(it.N), 0, 0};
       rows += it.N;
     }
     if (!launch_table(fmt, t, x_dtype, s, err)) return false;
