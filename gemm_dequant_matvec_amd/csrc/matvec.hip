@@ -24,6 +24,8 @@
 // R rows x B vectors are then reduced across the LPR lanes of the row with a
 // butterfly that halves the value count at every step, so the reduction costs
 // about R*B + log2(LPR) cross-lane exchanges instead of R*B*log2(LPR).
+#include <cstdlib>
+
 #include "qmv_internal.h"
 
 namespace qmv {
@@ -330,6 +332,16 @@ hipError_t pick_lpr(const uint8_t* W, const Planes& p, const void* x, float* y, 
 
 }  // namespace
 
+namespace {
+bool use_mfma() {
+  static const bool v = [] {
+    const char* e = getenv("QMV_MATVEC_MFMA");  // A/B comparison only: 0 = FMA kernel for batch >= 2
+    return !(e && e[0] == '0');
+  }();
+  return v;
+}
+}  // namespace
+
 hipError_t launch_matvec(int fmt, int64_t N, int64_t K, int64_t batch, const uint8_t* W,
                          const void* x, int x_dtype, float* y, hipStream_t s) {
   const Planes p = planes_of(fmt, N, K);
@@ -344,6 +356,10 @@ hipError_t launch_matvec(int fmt, int64_t N, int64_t K, int64_t batch, const uin
     const void* xb = static_cast<const uint8_t*>(x) + b0 * K * xel;
     float* yb = y + b0 * N;
     hipError_t e = hipSuccess;
+    if (nb >= 2 && use_mfma() && launch_matvec_mfma(fmt, N, K, nb, W, xb, x_dtype, yb, s, &e)) {
+      if (e != hipSuccess) return e;
+      continue;
+    }
     switch (fmt) {
       case QMV_Q8_0: e = pick_lpr<QMV_Q8_0, false>(W, p, xb, yb, int(N), int(K), nb, s); break;
       case QMV_W4A16_G64:

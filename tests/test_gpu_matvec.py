@@ -116,6 +116,30 @@ def test_matvec_parity(qmv, fmt, batch):
             assert r["ok"], (fmt, N, K, batch, xd, r)
 
 
+# K cases of the batched (2..8 vector) matrix-core path: one wave, 8 waves of 8
+# blocks, 24 blocks per wave with a ragged last wave (and, for W4A16 / Q8_0,
+# a ragged last chunk), the largest K it takes, and a K past it (other kernel)
+MFMA_K = {
+    "q8_0": [32, 2048, 2080, 6144, 6176],
+    "w4a16_g64": [64, 2048, 2112, 6144, 6208],
+    "q4k": [256, 2048, 3328, 6144, 6400],
+    "q6k": [256, 2048, 3328, 5632, 6400],
+}
+
+
+@pytest.mark.parametrize("fmt", wl.FORMATS)
+@pytest.mark.parametrize("kcase", range(5))
+@pytest.mark.parametrize("batch", [2, 8])
+def test_batched_matvec_k_ranges(qmv, fmt, kcase, batch):
+    K = MFMA_K[fmt][kcase]
+    N = 37 if K > 4096 else 133
+    w = wl.gen_weights(fmt, N, K, (22, kcase, batch))
+    for xd in XDT[fmt]:
+        x = wl.gen_x(K, batch, xd, (22, kcase, batch))
+        r, _, _ = check_matvec(qmv, fmt, w, x, xd)
+        assert r["ok"], (fmt, K, batch, xd, r)
+
+
 @pytest.mark.parametrize("fmt", wl.FORMATS)
 def test_one_hot_returns_dequantized_column_bit_exact(qmv, fmt):
     N, K = 70, wl.BLOCK[fmt] * 8 if fmt != "w4a16_g64" else 2048
