@@ -95,49 +95,59 @@ __device__ __forceinline__ bf16x8 sbyte8(uint32_t w0, uint32_t w1) {
 
 __device__ __forceinline__ float f16f(uint32_t bits) { return f16_bits_to_f32(bits & 0xFFFFu); }
 
-// Activations of vector `vec` at k = k0 .. k0 + 7 (f32 or f16 storage), as f32.
+// Activations at x + off .. + 7 (f32 or f16 storage), as f32; zero unless
+// `valid`.  The address must be inside x either way: the load is unconditional
+// (a branch per load would keep the compiler from bounding the set-up's loads
+// in flight).
 template <bool XF16>
 __device__ __forceinline__ void load_x8(const void* x, int64_t off, bool valid, float (&v)[8]) {
   if constexpr (XF16) {
-    u32x4 h = {0, 0, 0, 0};
-    if (valid) h = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + off);
+    const u32x4 h = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + off);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      v[2 * i] = f16_bits_to_f32(h[i] & 0xFFFFu);
-      v[2 * i + 1] = f16_bits_to_f32(h[i] >> 16);
+      v[2 * i] = valid ? f16_bits_to_f32(h[i] & 0xFFFFu) : 0.0f;
+      v[2 * i + 1] = valid ? f16_bits_to_f32(h[i] >> 16) : 0.0f;
     }
   } else {
-    f32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
-    if (valid) {
-      const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + off);
-      a = p[0];
-      b = p[1];
-    }
+    const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + off);
+    const f32x4 a = p[0], b = p[1];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      v[i] = a[i];
-      v[4 + i] = b[i];
+      v[i] = valid ? a[i] : 0.0f;
+      v[4 + i] = valid ? b[i] : 0.0f;
     }
   }
 }
 
-// ------------------------------------------------- per-format weight chunks
+// ------------------------------------------------- per-format weight staging
 //
-// A chunk is the weight data of CF<FMT> fragments of one row for one lane:
-// 8 (one Q4K super-block, four W4A16 groups, eight Q8_0 blocks) or 4 (half a
-// Q6K super-block, whose codes, high bits and scales take twice the registers).
+// Per tile, each wave moves its K slice of the 16 weight rows in chunks of
+// 256 k (one Q4K / Q6K super-block, four W4A16 groups, eight Q8_0 blocks):
+// coalesced 16-byte global loads into registers, then into the wave's own
+// LDS region, from where each lane reads its MFMA operands.  16-byte pieces
+// of a row are XOR-permuted by row so that the 64 lanes' operand reads of one
+// MFMA fall in distinct LDS banks.  LDS layout of a chunk (dwords):
+//   codes   rows of 32 dwords (Q8_0: 64); piece p of row r at
+//           32r + 4 (p ^ ((r / 2) % 8))   (Q8_0: 64r + 4 (p ^ r))
+//   aux     at 512 (Q8_0: 1024): W4A16 sz and Q8_0 scales [16][4];
+//           Q6K high bits [16][16] (piece p of row r at 16r + 4 (p ^ ((r / 4) % 4)))
+//           and Q6K sub-block scales [16][4] at 768.
 template <int FMT>
-constexpr int CF = (FMT == QMV_Q6K) ? 4 : 8;
+struct Stage;  // one chunk in flight, per lane
+template <>
+struct Stage<QMV_Q4K> { u32x4 q[2]; u32x4 meta; };
+template <>
+struct Stage<QMV_W4A16_G64> { u32x4 q[2]; uint32_t sz; };
+template <>
+struct Stage<QMV_Q8_0> { u32x4 q[4]; uint32_t sc; };
+template <>
+struct Stage<QMV_Q6K> { u32x4 ql[2]; u32x4 qh; uint32_t s; uint32_t d; };
+
 template <int FMT>
-struct Chunk;
-template <>
-struct Chunk<QMV_Q4K> { uint32_t q[8]; u32x4 meta; };
-template <>
-struct Chunk<QMV_W4A16_G64> { u32x2 q[4]; uint32_t sz[4]; };
-template <>
-struct Chunk<QMV_Q8_0> { u32x2 q[8]; uint32_t sc[8]; };
-template <>
-struct Chunk<QMV_Q6K> { uint32_t ql[4][2]; u32x2 qh[4]; u32x2 s; uint32_t d; };
+constexpr int kStageDw = FMT == QMV_Q8_0 ? 1024 + 64 : FMT == QMV_Q6K ? 512 + 256 + 64 : FMT == QMV_W4A16_G64 ? 512 + 64 : 512;
+
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int swz4(int r) { return (r >> 2) & 3; }
 
 __device__ __forceinline__ f32x4 mfma32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -153,69 +163,117 @@ __device__ __forceinline__ bf16x8 ones8() {
   return o;
 }
 
-// One 16-row tile seen from one lane: its weight row and plane addressing.
 template <int FMT>
-struct Tile {
+struct Staging {
   const MfmaArgs& a;
-  int64_t row;
-  const uint8_t* qrow;
-  int U, nsb, G;
+  int U, nsb, lane;
 
-  // weights of fragments u .. u + 7 (clamped into the row; fragments past K are
-  // never multiplied)
-  __device__ __forceinline__ Chunk<FMT> load(int u) const {
-    Chunk<FMT> c;
-    if constexpr (FMT == QMV_Q4K) {
+  // chunk of 256 k starting at fragment u, rows tile * 16 .. + 15 (clamped to
+  // N - 1).  Wave-uniform chunk bases and 32-bit per-lane offsets (packed
+  // matrices on this path stay below 2 GiB).  Where a chunk runs past the end
+  // of a row (W4A16 / Q8_0 with K not a multiple of 256), its blocks are
+  // clamped to the row's last block and never multiplied.
+  __device__ __forceinline__ Stage<FMT> load(int tile, int u) const {
+    Stage<FMT> st;
+    const uint32_t K = a.K;
+    auto row = [&](int i) { return uint32_t(min(tile * 16 + i, a.N - 1)); };
+    auto ld4 = [](const uint8_t* base, uint32_t off) {
+      return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + off));
+    };
+    if constexpr (FMT == QMV_Q4K || FMT == QMV_Q6K) {
+      const int sb = u >> 3;
+      const uint8_t* qb = a.W + 128 * sb;
 #pragma unroll
-      for (int f = 0; f < 8; ++f) {
-        const int uu = min(u + f, U - 1);
-        c.q[f] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(qrow + 16 * uu + 4 * G));
+      for (int i = 0; i < 2; ++i) {
+        const uint32_t off = row(8 * i + (lane >> 3)) * (K >> 1) + 16 * (lane & 7);
+        if constexpr (FMT == QMV_Q4K) st.q[i] = ld4(qb, off); else st.ql[i] = ld4(qb, off);
       }
-      c.meta = reinterpret_cast<const u32x4*>(a.W + a.off1)[row * nsb + (u >> 3)];
+      if constexpr (FMT == QMV_Q4K) {
+        st.meta = *reinterpret_cast<const u32x4*>(a.W + a.off1 + 16 * sb + row(lane & 15) * (16 * uint32_t(nsb)));
+      } else {
+        const uint32_t r4 = row(lane >> 2);
+        st.qh = ld4(a.W + a.off1 + 64 * sb, r4 * (K >> 2) + 16 * (lane & 3));
+        st.s = *reinterpret_cast<const uint32_t*>(a.W + a.off2 + 16 * sb + r4 * (K >> 4) + 4 * (lane & 3));
+        st.d = *reinterpret_cast<const uint16_t*>(a.W + a.off3 + 2 * sb + row(lane & 15) * (2 * uint32_t(nsb)));
+      }
     } else if constexpr (FMT == QMV_W4A16_G64) {
-      const int ng = a.K >> 6;
+      const int ng = K >> 6, g0 = u >> 1;
+      const bool full = g0 + 4 <= ng;  // wave-uniform
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int gi = min((u >> 1) + g, ng - 1);
-        c.q[g] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(qrow + 32 * gi + 8 * G));
-        c.sz[g] = reinterpret_cast<const uint32_t*>(a.W + a.off1)[row * ng + gi];
+      for (int i = 0; i < 2; ++i) {
+        const int pc = lane & 7;
+        const uint32_t rb = row(8 * i + (lane >> 3)) * (K >> 1);
+        if (full) {
+          st.q[i] = ld4(a.W + 32 * g0, rb + 16 * pc);
+        } else {
+          const int g = min(g0 + (pc >> 1), ng - 1);
+          st.q[i] = ld4(a.W, rb + 32 * g + 16 * (pc & 1));
+        }
       }
-    } else if constexpr (FMT == QMV_Q8_0) {
+      st.sz = *reinterpret_cast<const uint32_t*>(a.W + a.off1 +
+                                                 4 * (row(lane >> 2) * uint32_t(ng) + min(g0 + (lane & 3), ng - 1)));
+    } else {  // Q8_0
+      const bool full = u + 8 <= U;  // wave-uniform
 #pragma unroll
-      for (int f = 0; f < 8; ++f) {
-        const int uu = min(u + f, U - 1);
-        c.q[f] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(qrow + 32 * uu + 8 * G));
-        c.sc[f] = reinterpret_cast<const uint16_t*>(a.W + a.off1)[row * U + uu];
+      for (int i = 0; i < 4; ++i) {
+        const int pc = lane & 15;
+        const uint32_t rb = row(4 * i + (lane >> 4)) * K;
+        if (full) {
+          st.q[i] = ld4(a.W + 32 * u, rb + 16 * pc);
+        } else {
+          const int bk = min(u + (pc >> 1), U - 1);
+          st.q[i] = ld4(a.W, rb + 32 * bk + 16 * (pc & 1));
+        }
       }
-    } else {
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        const int uu = min(u + f, U - 1);
-        const uint32_t* w = reinterpret_cast<const uint32_t*>(qrow + 16 * uu);
-        c.ql[f][0] = __builtin_nontemporal_load(w + (G >> 1));
-        c.ql[f][1] = __builtin_nontemporal_load(w + 2 + (G >> 1));
-        c.qh[f] = reinterpret_cast<const u32x2*>(a.W + a.off1)[row * U + uu];
-      }
-      // 8 int8 scales: sub-blocks 2u .. 2u + 7 (u is a multiple of 4)
-      c.s = reinterpret_cast<const u32x2*>(a.W + a.off2)[(row * U + u) >> 2];
-      c.d = reinterpret_cast<const uint16_t*>(a.W + a.off3)[row * nsb + (u >> 3)];
+      const uint16_t* sp = reinterpret_cast<const uint16_t*>(a.W + a.off1) + row(lane >> 2) * uint32_t(U);
+      const int j = u + 2 * (lane & 3);
+      st.sc = uint32_t(sp[min(j, U - 1)]) | (uint32_t(sp[min(j + 1, U - 1)]) << 16);
     }
-    return c;
+    return st;
   }
 
-  // acc += this chunk's contribution for vectors 2G (acc0) and 2G + 1 (acc1)
-  __device__ __forceinline__ void compute(const Chunk<FMT>& c, const bf16x8* A, int u, float& acc0,
-                                          float& acc1) const {
+  __device__ __forceinline__ void store(const Stage<FMT>& st, uint32_t* lds) const {
+    if constexpr (FMT == QMV_Q8_0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * i + (lane >> 4), p = lane & 15;
+        *reinterpret_cast<u32x4*>(lds + 64 * r + 4 * (p ^ r)) = st.q[i];
+      }
+      lds[1024 + 4 * (lane >> 2) + (lane & 3)] = st.sc;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = 8 * i + (lane >> 3), p = lane & 7;
+        u32x4 v;
+        if constexpr (FMT == QMV_Q6K) v = st.ql[i]; else v = st.q[i];
+        *reinterpret_cast<u32x4*>(lds + 32 * r + 4 * (p ^ swz8(r))) = v;
+      }
+      if constexpr (FMT == QMV_W4A16_G64) {
+        lds[512 + 4 * (lane >> 2) + (lane & 3)] = st.sz;
+      } else if constexpr (FMT == QMV_Q6K) {
+        const int r = lane >> 2, p = lane & 3;
+        *reinterpret_cast<u32x4*>(lds + 512 + 16 * r + 4 * (p ^ swz4(r))) = st.qh;
+        lds[768 + 4 * r + p] = st.s;
+      }
+    }
+  }
+
+  // acc += the chunk's contribution (fragments u .. u + 7 of this wave's
+  // operands A) for vectors 2G (acc0) and 2G + 1 (acc1) of row r = lane & 15
+  __device__ __forceinline__ void compute(const Stage<FMT>& st, const uint32_t* lds, const bf16x8* A, int u,
+                                          float& acc0, float& acc1) const {
+    const int r = lane & 15, G = lane >> 4;
     const f32x4 z = {0, 0, 0, 0};
     const bf16x8 ones = ones8();
     if constexpr (FMT == QMV_Q4K) {
-      const float d = f16f(c.meta[0]), dmin = f16f(c.meta[0] >> 16);
-      const uint64_t lo = uint64_t(c.meta[1]) | (uint64_t(c.meta[2]) << 32);
-      const uint64_t hi = uint64_t(c.meta[2] >> 16) | (uint64_t(c.meta[3]) << 16);
+      const u32x4 m = st.meta;
+      const float d = f16f(m[0]), dmin = f16f(m[0] >> 16);
+      const uint64_t lo = uint64_t(m[1]) | (uint64_t(m[2]) << 32);
+      const uint64_t hi = uint64_t(m[2] >> 16) | (uint64_t(m[3]) << 16);
 #pragma unroll
       for (int f = 0; f < 8; ++f) {
-        if (u + f >= U) break;
-        const f32x4 dq = mfma32(A[f], nib8(c.q[f]), z);
+        const uint32_t w = lds[32 * r + 4 * (f ^ swz8(r)) + G];
+        const f32x4 dq = mfma32(A[f], nib8(w), z);
         const f32x4 dx = mfma32(A[f], ones, z);
         const float ds = d * static_cast<float>(static_cast<uint32_t>(lo >> (6 * f)) & 63u);
         const float dm = dmin * static_cast<float>(static_cast<uint32_t>(hi >> (6 * f)) & 63u);
@@ -224,46 +282,51 @@ struct Tile {
         acc1 = fmaf(-dm, s1, fmaf(ds, fmaf(-128.0f, s1, dq[2] + dq[3]), acc1));
       }
     } else if constexpr (FMT == QMV_W4A16_G64) {
+      const u32x4 sz = *reinterpret_cast<const u32x4*>(lds + 512 + 4 * r);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         if (u + 2 * g >= U) break;
-        const f32x4 dq = mfma32(A[2 * g + 1], nib8(c.q[g][1]), mfma32(A[2 * g], nib8(c.q[g][0]), z));
+        const u32x2 w = *reinterpret_cast<const u32x2*>(lds + 32 * r + 4 * ((2 * g + (G >> 1)) ^ swz8(r)) + 2 * (G & 1));
+        const f32x4 dq = mfma32(A[2 * g + 1], nib8(w[1]), mfma32(A[2 * g], nib8(w[0]), z));
         const f32x4 dx = mfma32(A[2 * g + 1], ones, mfma32(A[2 * g], ones, z));
-        const float s = f16f(c.sz[g]), zr = f16f(c.sz[g] >> 16);
+        const float s = f16f(sz[g]), zr = f16f(sz[g] >> 16);
         const float s0 = dx[0] + dx[1], s1 = dx[2] + dx[3];
         acc0 = fmaf(s, fmaf(-zr, s0, fmaf(-128.0f, s0, dq[0] + dq[1])), acc0);
         acc1 = fmaf(s, fmaf(-zr, s1, fmaf(-128.0f, s1, dq[2] + dq[3])), acc1);
       }
     } else if constexpr (FMT == QMV_Q8_0) {
+      const u32x4 sc = *reinterpret_cast<const u32x4*>(lds + 1024 + 4 * r);
 #pragma unroll
       for (int f = 0; f < 8; ++f) {
         if (u + f >= U) break;
-        const f32x4 dq = mfma32(A[f], sbyte8(c.q[f][0], c.q[f][1]), z);
+        const u32x2 w = *reinterpret_cast<const u32x2*>(lds + 64 * r + 4 * ((2 * f + (G >> 1)) ^ r) + 2 * (G & 1));
+        const f32x4 dq = mfma32(A[f], sbyte8(w[0], w[1]), z);
         const f32x4 dx = mfma32(A[f], ones, z);
-        const float s = f16f(c.sc[f]);
+        const float s = f16f(sc[f >> 1] >> (16 * (f & 1)));
         acc0 = fmaf(s, fmaf(-128.0f, dx[0] + dx[1], dq[0] + dq[1]), acc0);
         acc1 = fmaf(s, fmaf(-128.0f, dx[2] + dx[3], dq[2] + dq[3]), acc1);
       }
-    } else {
+    } else {  // Q6K
       const int sh_q = 4 * (G & 1);
       const int sh_h = 4 * (G >> 1) + 2 * (G & 1);
       const s16x4 ones4 = {0x3F80, 0x3F80, 0x3F80, 0x3F80};
-      const float d = f16f(c.d);
+      const float d = f16f(st.d);
+      const u32x4 sv = *reinterpret_cast<const u32x4*>(lds + 768 + 4 * r);
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        if (u + f >= U) break;
+      for (int f = 0; f < 8; ++f) {
         const u32x4 aw = __builtin_bit_cast(u32x4, A[f]);
+        const u32x2 hw = *reinterpret_cast<const u32x2*>(lds + 512 + 16 * r + 4 * ((f >> 1) ^ swz4(r)) + 2 * (f & 1));
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          const uint32_t v = ((c.ql[f][s] >> sh_q) & 0x0F0F0F0Fu) | (((c.qh[f][s] >> sh_h) & 0x03030303u) << 4);
+          const uint32_t qlw = lds[32 * r + 4 * (f ^ swz8(r)) + 2 * s + (G >> 1)];
+          const uint32_t v = ((qlw >> sh_q) & 0x0F0F0F0Fu) | (((hw[s] >> sh_h) & 0x03030303u) << 4);
           const u32x2 bw = {code_pair<0x04010400u>(v), code_pair<0x04030402u>(v)};
           const u32x2 aa = {aw[2 * s], aw[2 * s + 1]};
           const s16x4 a4 = __builtin_bit_cast(s16x4, aa);
           const f32x4 dq = mfma16(a4, __builtin_bit_cast(s16x4, bw));
           const f32x4 dx = mfma16(a4, ones4);
-          const int j = 2 * f + s;  // sub-block within the chunk
-          const float sc = static_cast<float>(static_cast<int8_t>((c.s[j >> 2] >> (8 * (j & 3))) & 0xFFu));
-          const float ds = d * sc;
+          const int j = 2 * f + s;  // sub-block within the super-block
+          const float ds = d * static_cast<float>(static_cast<int8_t>((sv[j >> 2] >> (8 * (j & 3))) & 0xFFu));
           acc0 = fmaf(ds, fmaf(-160.0f, dx[0] + dx[1], dq[0] + dq[1]), acc0);
           acc1 = fmaf(ds, fmaf(-160.0f, dx[2] + dx[3], dq[2] + dq[3]), acc1);
         }
@@ -276,7 +339,7 @@ struct Tile {
 //
 // Per-format k order of fragment u (32 k of K), lane group G = lane >> 4:
 //   Q8_0, Q4K   k = 32u + 8G + e                 (e = 0..7: the lane's 8 bytes / one nibble word)
-//   W4A16       k = 64(u/2) + 16G + 8(u%2) + e    (one 8-byte load per lane serves both halves
+//   W4A16       k = 64(u/2) + 16G + 8(u%2) + e    (one 8-byte read per lane serves both halves
 //                                                  of the 64-k group)
 //   Q6K         two 16x16x16 MFMAs, sub-block s = 0, 1:
 //               k = 32u + 16s + 8(G/2) + 2e + G%2  (e = 0..3: one byte lane of one 6-bit code
@@ -284,7 +347,7 @@ struct Tile {
 template <int FMT, bool XF16, int KF>
 __global__ __launch_bounds__(64 * kMaxWaves) void matvec_mfma_kernel(const MfmaArgs a) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: chunk bases in SGPRs
   const int G = lane >> 4;
   const int p = lane & 15;  // A row: part p = 2 * vector + low
   const int vec = p >> 1;
@@ -294,6 +357,17 @@ __global__ __launch_bounds__(64 * kMaxWaves) void matvec_mfma_kernel(const MfmaA
   const int u0 = wave * KF;
   const bool vec_ok = vec < a.nv;
   const int64_t xrow = int64_t(min(vec, a.nv - 1)) * K;  // address stays inside x for padding parts
+  const int ntiles = (N + 15) >> 4;
+  const Staging<FMT> stg{a, U, K >> 8, lane};
+
+  __shared__ uint32_t stage_lds[kMaxWaves][kStageDw<FMT>];
+  __shared__ f32x4 red_raw[2][kMaxWaves][32];  // [buffer][wave][lane pair] -> 2 x float2
+  uint32_t* lds = stage_lds[wave];
+  float* red = reinterpret_cast<float*>(red_raw);
+
+  // first chunk of the first tile in flight before the activations are set up
+  int tile = blockIdx.x;  // < ntiles (grid <= ntiles)
+  Stage<FMT> R = stg.load(tile, u0);
 
   // ---- A operands of this wave's K slice, built once (zero past K and for
   // vectors >= nv, so those fragments and parts contribute nothing)
@@ -301,57 +375,44 @@ __global__ __launch_bounds__(64 * kMaxWaves) void matvec_mfma_kernel(const MfmaA
 #pragma unroll
   for (int f = 0; f < KF; ++f) {
     const int u = u0 + f;
+    const int uc = min(u, U - 1);
     const bool ok = vec_ok && u < U;
     float v[8];
-    if constexpr (FMT == QMV_Q6K) {  // f32 x only: k = 32u + 16s + 8(G/2) + (G%2) + 2e
-      const float* xp = static_cast<const float*>(a.x) + xrow + 32 * min(u, U - 1) + 8 * (G >> 1) + (G & 1);
+    if constexpr (FMT == QMV_Q6K) {  // f32 x: k = 32u + 16s + 8(G/2) + (G%2) + 2e
+      const uint32_t odd = 0u - static_cast<uint32_t>(G & 1);
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
+      for (int s = 0; s < 2; ++s) {
+        float t[8];
+        load_x8<false>(a.x, xrow + 32 * uc + 16 * s + 8 * (G >> 1), ok, t);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[4 * s + e] = ok ? xp[16 * s + 2 * e] : 0.0f;
+        for (int e = 0; e < 4; ++e)  // odd or even element by mask (a select would become a lane-varying index)
+          v[4 * s + e] = __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, t[2 * e + 1]) & odd) |
+                                                       (__builtin_bit_cast(uint32_t, t[2 * e]) & ~odd));
+      }
     } else {
-      const int uc = min(u, U - 1);
       const int k0 = (FMT == QMV_W4A16_G64) ? 64 * (uc >> 1) + 16 * G + 8 * (uc & 1) : 32 * uc + 8 * G;
       load_x8<XF16>(a.x, xrow + k0, ok, v);
     }
     A[f] = as_bf8(part_pair(v[0], v[1], low), part_pair(v[2], v[3], low), part_pair(v[4], v[5], low),
                   part_pair(v[6], v[7], low));
-    // at most 8 fragments' raw activations in flight (register peak of the set-up)
-    if ((f & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+    if ((f & 7) == 7) __builtin_amdgcn_sched_barrier(0);  // at most 8 fragments' raw activations live
   }
-  __shared__ f32x4 red_raw[2][kMaxWaves][32];  // [buffer][wave][lane pair] -> 2 x float2
-  float* red = reinterpret_cast<float*>(red_raw);
-  const int ntiles = (N + 15) >> 4;
-  const int64_t rowbytes_q = (FMT == QMV_Q8_0) ? K : (K >> 1);
-  const int nsb = K >> 8;  // super-blocks per row (Q4K, Q6K)
-  int buf = 0;
 
-  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const int64_t row = min(tile * 16 + p, N - 1);  // B column j = lane & 15 = weight row
-    const uint8_t* qrow = a.W + row * rowbytes_q;
+  const int nch = (min(KF, U - u0) + 7) >> 3;  // chunks of this wave (>= 1)
+  int buf = 0;
+  for (;;) {
     float acc0 = 0.0f, acc1 = 0.0f;  // vectors 2G and 2G + 1 of weight row (lane & 15)
-    const Tile<FMT> t{a, row, qrow, U, nsb, G};
-    // two-stage pipeline over chunks: the next chunk's weights are in flight
-    // while the current one is multiplied
-    // (single stage where two chunks would not fit in registers next to 24 A
-    // operands: Q6K and Q8_0 at K > 2048)
-    constexpr int C = CF<FMT>;
-    constexpr bool PIPE = !(KF > 8 && (FMT == QMV_Q6K || FMT == QMV_Q8_0));
-    Chunk<FMT> cur = t.load(u0);
 #pragma unroll
-    for (int c = 0; c < KF; c += C) {
-      if (u0 + c >= U) break;
-      if constexpr (PIPE) {
-        Chunk<FMT> nxt;
-        if (c + C < KF && u0 + c + C < U) nxt = t.load(u0 + c + C);
-        __builtin_amdgcn_sched_barrier(0);
-        t.compute(cur, A + c, u0 + c, acc0, acc1);
-        cur = nxt;
-      } else {
-        if (c > 0) cur = t.load(u0 + c);
-        t.compute(cur, A + c, u0 + c, acc0, acc1);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    for (int c = 0; c < KF / 8; ++c) {
+      if (c >= nch) break;
+      stg.store(R, lds);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const Stage<FMT> cur = R;
+      // next chunk: the following one of this tile, else the first of the next tile
+      if (c + 1 < nch) R = stg.load(tile, u0 + 8 * (c + 1));
+      else if (tile + int(gridDim.x) < ntiles) R = stg.load(tile + gridDim.x, u0);
+      stg.compute(cur, lds, A + 8 * c, u0 + 8 * c, acc0, acc1);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // operand reads done before the next store
     }
 
     // ---- the W partial sums of this tile meet in LDS, added in wave order
@@ -369,6 +430,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void matvec_mfma_kernel(const MfmaA
       if (v < a.nv && r < N) a.y[int64_t(v) * N + r] = s;
     }
     buf ^= 1;
+    tile += gridDim.x;
+    if (tile >= ntiles) break;
   }
 }
 
@@ -405,10 +468,11 @@ bool pick_kf(MfmaArgs& a, hipStream_t s, hipError_t* err) {
 }  // namespace
 
 // 2..8 vectors on the matrix cores.  Returns false (nothing launched) for
-// shapes outside this kernel's range (K > 6144).
+// shapes outside this kernel's range (K > 6144, packed matrix >= 2 GiB).
 bool launch_matvec_mfma(int fmt, int64_t N, int64_t K, int nv, const uint8_t* W, const void* x, int x_dtype,
                         float* y, hipStream_t s, hipError_t* err) {
   const Planes p = planes_of(fmt, N, K);
+  if (p.total >= (int64_t(1) << 31)) return false;  // the kernel addresses planes with 32-bit offsets
   MfmaArgs a{W, p.off[1], p.off[2], p.off[3], x, y, int(N), int(K), nv, 0};
   const bool f16 = (x_dtype == QMV_F16);
   switch (fmt) {
