@@ -389,8 +389,21 @@ def gemm_leg(qmv, M, reps=20):
             qmv.matvec(fmt, W, Xf, N, K, y=ymv)
     ms_mv, _ = time_graph(run_mv, 5, 2)
     ms_mv /= reps
+    # context: the vendor bf16 GEMM (torch.matmul -> hipBLASLt) on the same matrix
+    # dequantized to a dense bf16 copy (3.5x the weight bytes; not this library's path)
+    # (a contiguous [K][N] copy: no transposed view is handed to the library)
+    WdT = qmv.dequant(fmt, W, N, K).to(torch.bfloat16).t().contiguous()
+    Yd = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def run_blas():
+        for _ in range(reps):
+            torch.matmul(X, WdT, out=Yd)
+    ms_bl, _ = time_graph(run_blas, 5, 2)
+    ms_bl /= reps
+    del WdT
     return {"us": ms * 1e3, "tflops": tf, "frac_bf16_peak": tf / BF16_PEAK_TFLOPS,
-            "matvec_path_us": ms_mv * 1e3}
+            "matvec_path_us": ms_mv * 1e3, "dense_bf16_library_gemm_us": ms_bl * 1e3,
+            "dense_bf16_library_frac_peak": flops / (ms_bl * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
 
 
 def cpu_baseline(st, seconds):

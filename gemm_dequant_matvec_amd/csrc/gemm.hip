@@ -20,10 +20,10 @@
 //     never touches LDS.
 //   * The bf16 token tile goes through LDS (two buffers, one barrier per step),
 //     in 128-byte rows: the 8-k chunk 4g + s of a token row is stored in half
-//     s >> 1 at chunk 4 (s & 1) + (g ^ (row & 3)), so the 4 lane groups of MFMA s
-//     read 4 adjacent chunks of 16 consecutive rows, XOR-swizzled by row -- a
-//     pattern gfx950 serves at close to full LDS bandwidth (measured ~260
-//     B/clk/CU; 144-byte padded rows gave ~110).
+//     s >> 1 at chunk (4 (s & 1) + g) ^ ((row / 2) % 8), so the 16 lanes of one
+//     ds_read_b128 pass (16 consecutive rows) hit 16 distinct groups of 4 banks
+//     (an XOR by row % 4 left 4-way conflicts; 144-byte padded rows served ~110
+//     B/clk/CU where swizzled 128-byte rows reach ~260).
 //   * Weight loads for S - 1 steps ahead are in flight (register stages); the
 //     K loop is unrolled in chunks so that no load is pending across a loop
 //     back-edge (the compiler drains every load at such an edge).
@@ -63,13 +63,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 
 // 8 weights (one 32-bit word of nibbles, k in order) -> bf16x8 A operand.
+// Even and odd nibbles are split with two masks, so every code is a byte that
+// converts to f32 in one instruction (v_cvt_f32_ubyteN).
 __device__ __forceinline__ bf16x8 dequant8(uint32_t wd, float s, float c) {
+  const uint32_t ev = wd & 0x0F0F0F0Fu;         // byte b: q[2b]
+  const uint32_t od = (wd >> 4) & 0x0F0F0F0Fu;  // byte b: q[2b + 1]
   uint32_t o[4];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const uint32_t byte = (wd >> (8 * b)) & 0xFFu;  // k = 2b (low nibble), 2b + 1 (high)
-    o[b] = pack_bf16x2(fmaf(s, static_cast<float>(byte & 15u), c), fmaf(s, static_cast<float>(byte >> 4), c));
-  }
+  for (int b = 0; b < 4; ++b)
+    o[b] = pack_bf16x2(fmaf(s, static_cast<float>((ev >> (8 * b)) & 0xFFu), c),
+                       fmaf(s, static_cast<float>((od >> (8 * b)) & 0xFFu), c));
   return __builtin_bit_cast(bf16x8, u32x4{o[0], o[1], o[2], o[3]});
 }
 
@@ -149,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void gemm_w4g64_kernel(
       const int id = p * kThreads + tid;
       const int r = id >> 4, c16 = id & 15;
       const int gg = c16 >> 2, ss = c16 & 3;  // k = 32 gg + 8 ss
-      Xs[buf][ss >> 1][r][4 * (ss & 1) + (gg ^ (r & 3))] = xr[p];
+      Xs[buf][ss >> 1][r][(4 * (ss & 1) + gg) ^ ((r >> 1) & 7)] = xr[p];
     }
   };
 
@@ -175,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void gemm_w4g64_kernel(
     auto read_b = [&](bf16x8 (&b)[FM], int s) {
 #pragma unroll
       for (int j = 0; j < FM; ++j)
-        b[j] = __builtin_bit_cast(bf16x8, Xs[buf][s >> 1][16 * j + fr][4 * (s & 1) + (g ^ (fr & 3))]);
+        b[j] = __builtin_bit_cast(bf16x8, Xs[buf][s >> 1][16 * j + fr][(4 * (s & 1) + g) ^ ((fr >> 1) & 7)]);
     };
     bf16x8 b0[FM], b1[FM];
     read_b(b0, 0);
