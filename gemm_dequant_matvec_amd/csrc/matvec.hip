@@ -333,13 +333,16 @@ hipError_t pick_lpr(const uint8_t* W, const Planes& p, const void* x, float* y, 
 }  // namespace
 
 namespace {
-bool use_mfma() {
-  static const bool v = [] {
-    const char* e = getenv("QMV_MATVEC_MFMA");  // A/B comparison only: 0 = FMA kernel for batch >= 2
-    return !(e && e[0] == '0');
+// A/B comparison only: QMV_MATVEC_MFMA=0 sends batch >= 2 to the FMA kernel,
+// =2 also sends batch 1 to the matrix-core kernel.
+int mfma_mode() {
+  static const int v = [] {
+    const char* e = getenv("QMV_MATVEC_MFMA");
+    return e ? atoi(e) : 1;
   }();
   return v;
 }
+bool use_mfma() { return mfma_mode() != 0; }
 }  // namespace
 
 hipError_t launch_matvec(int fmt, int64_t N, int64_t K, int64_t batch, const uint8_t* W,
@@ -349,6 +352,7 @@ hipError_t launch_matvec(int fmt, int64_t N, int64_t K, int64_t batch, const uin
   const size_t xel = f16 ? 2 : 4;
   if (batch == 1) {
     hipError_t e = hipSuccess;
+    if (mfma_mode() == 2 && launch_matvec_mfma(fmt, N, K, 1, W, x, x_dtype, y, s, &e)) return e;
     if (launch_matvec_b1(fmt, N, K, W, x, x_dtype, y, s, &e)) return e;
   }
   for (int64_t b0 = 0; b0 < batch; b0 += 8) {

@@ -27,12 +27,6 @@ constexpr int kThreads = 64 * kWaves;
 typedef __attribute__((ext_vector_type(2))) _Float16 half2_t;
 
 __device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
-__device__ __forceinline__ float byte_f32(uint32_t v, int c) {
-  return static_cast<float>((v >> (8 * c)) & 0xFFu);
-}
-__device__ __forceinline__ float sbyte_f32(uint32_t v, int c) {
-  return static_cast<float>(static_cast<int32_t>(v << (24 - 8 * c)) >> 24);
-}
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -213,15 +207,23 @@ __device__ __forceinline__ float unit_dot(const Raw<FMT>& w, const XUnit<FMT == 
     const float zo = 1024.0f + f16_bits_to_f32(w.sz >> 16);  // exact
     return fmaf(s, fmaf(-zo, xu.s, dot), acc);
   } else if constexpr (FMT == QMV_Q8_0) {
-    float qx = 0.0f;
+    // code u = q + 128 as t = 0.5 + u / 65536 (u in mantissa bits 8..15 of 0.5)
+    float tx = 0.0f;
     const uint32_t wd[8] = {w.q0.x, w.q0.y, w.q0.z, w.q0.w, w.q1.x, w.q1.y, w.q1.z, w.q1.w};
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t u = wd[i] ^ 0x80808080u;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) qx = fmaf(sbyte_f32(wd[i], c), xu.v[4 * i + c], qx);
-    return fmaf(f16_bits_to_f32(w.sc), qx, acc);
+      for (int c = 0; c < 4; ++c)
+        tx = fmaf(__builtin_bit_cast(float, __builtin_amdgcn_perm(0x3F000000u, u, 0x070C000Cu | (c << 8))),
+                  xu.v[4 * i + c], tx);
+    }
+    const float ux = 65536.0f * fmaf(-0.5f, xu.s0, tx);  // sum (q + 128) x
+    return fmaf(f16_bits_to_f32(w.sc), fmaf(-128.0f, xu.s0, ux), acc);
   } else {
-    float qa = 0.0f, qb = 0.0f;
+    // 4- and 6-bit codes b as t = 0.5 + b / 256 (b in mantissa bits 16..21 of
+    // 0.5, placed by one v_perm_b32): sum b x = 256 (sum t x - sum x / 2)
+    float ta = 0.0f, tb = 0.0f;
     const uint32_t wd[4] = {w.q.x, w.q.y, w.q.z, w.q.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -233,14 +235,17 @@ __device__ __forceinline__ float unit_dot(const Raw<FMT>& w, const XUnit<FMT == 
         ev |= ((h >> (2 * f)) & 0x03030303u) << 4;
         od |= ((h >> (2 * f + 2)) & 0x03030303u) << 4;
       }
-      float t = (FMT == QMV_Q6K && i >= 2) ? qb : qa;
+      float t = (FMT == QMV_Q6K && i >= 2) ? tb : ta;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        t = fmaf(byte_f32(ev, c), xu.v[8 * i + 2 * c], t);
-        t = fmaf(byte_f32(od, c), xu.v[8 * i + 2 * c + 1], t);
+        const uint32_t sel = 0x07000C0Cu | (uint32_t(c) << 16);
+        t = fmaf(__builtin_bit_cast(float, __builtin_amdgcn_perm(0x3F000000u, ev, sel)), xu.v[8 * i + 2 * c], t);
+        t = fmaf(__builtin_bit_cast(float, __builtin_amdgcn_perm(0x3F000000u, od, sel)), xu.v[8 * i + 2 * c + 1], t);
       }
-      if (FMT == QMV_Q6K && i >= 2) qb = t; else qa = t;
+      if (FMT == QMV_Q6K && i >= 2) tb = t; else ta = t;
     }
+    const float qa = 256.0f * fmaf(-0.5f, xu.s0, ta);  // sum b x (Q6K: k < 16)
+    const float qb = 256.0f * fmaf(-0.5f, xu.s1, tb);  // Q6K: k >= 16
     if constexpr (FMT == QMV_W4A16_G64) {
       const float s = f16_bits_to_f32(w.sz & 0xFFFFu), z = f16_bits_to_f32(w.sz >> 16);
       return fmaf(s, fmaf(-z, xu.s0, qa), acc);
@@ -308,7 +313,8 @@ __global__ __launch_bounds__(kThreads) void matvec_xs_kernel(const SegTable t) {
   const int N = sg.N;
   float* __restrict__ y = sg.y;
   const int ngroups = (N + R * RPW - 1) / (R * RPW);
-  const int gw = (int(blockIdx.x) - sg.b0) * kWaves + (threadIdx.x >> 6);
+  // wave-uniform (readfirstlane): the loop's branches and loads stay scalar-controlled
+  const int gw = (int(blockIdx.x) - sg.b0) * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int TW = sg.nb * kWaves;
 
   int uu[UPL], sh[UPL];
@@ -321,8 +327,7 @@ __global__ __launch_bounds__(kThreads) void matvec_xs_kernel(const SegTable t) {
     sh[j] = 6 * (uu[j] & 7);
   }
 
-  int grp = gw;
-  Raw<FMT> cur[R][UPL];
+  Raw<FMT> ga[R][UPL], gb[R][UPL];  // two register sets, used in turn (no copies)
   auto load_group = [&](Raw<FMT> (&dst)[R][UPL], int gi) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -331,16 +336,14 @@ __global__ __launch_bounds__(kThreads) void matvec_xs_kernel(const SegTable t) {
       for (int j = 0; j < UPL; ++j) dst[r][j] = load_raw<FMT>(g, row, uu[j]);
     }
   };
-  if (grp < ngroups) load_group(cur, grp);
+  int grp = gw;
+  if (grp < ngroups) load_group(ga, grp);
 
   XUnit<H2> xs[UPL];
 #pragma unroll
   for (int j = 0; j < UPL; ++j) load_x<FMT, XF16>(xs[j], sg.x, 32 * uu[j], uv[j]);
 
-  for (; grp < ngroups; grp += TW) {
-    Raw<FMT> nxt[R][UPL];
-    const int gn = grp + TW;
-    if (gn < ngroups) load_group(nxt, gn);
+  auto do_group = [&](const Raw<FMT> (&cur)[R][UPL], int gi) {
     float acc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = 0.0f;
@@ -354,20 +357,23 @@ __global__ __launch_bounds__(kThreads) void matvec_xs_kernel(const SegTable t) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const float tot = group_sum<LPR>(acc[r], sub);
-      const int row = grp * (R * RPW) + r * RPW + sub;
+      const int row = gi * (R * RPW) + r * RPW + sub;
       if (l == 0 && row < N) y[row] = tot;
     }
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int j = 0; j < UPL; ++j) cur[r][j] = nxt[r][j];
+  };
+  // the next group's loads are in flight while the current one is reduced
+  while (grp < ngroups) {
+    const int g1 = grp + TW;
+    if (g1 < ngroups) load_group(gb, g1);
+    do_group(ga, grp);
+    if (g1 >= ngroups) break;
+    const int g2 = g1 + TW;
+    if (g2 < ngroups) load_group(ga, g2);
+    do_group(gb, g1);
+    grp = g2;
   }
 }
 
-// Blocks per segment: the whole launch is capped at 16 waves per CU on 256
-// CUs (each wave then walks several row groups); each segment gets a share
-// in proportion to its row groups, at least one block and no more blocks
-// than it has groups to hand out.
 template <int FMT, bool XF16, int LPR, int UPL, int R>
 hipError_t go(SegTable& t, hipStream_t s) {
   constexpr int rows_per_group = R * (64 / LPR);
