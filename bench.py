@@ -349,7 +349,7 @@ class Sweep:
             else:
                 self.calls.append((fmt, K, [item]))
             prev = (share, fmt, K)
-        self.launches = len(self.calls) if batch == 1 else sum(len(c[2]) for c in self.calls)
+        self.launches = len(self.calls)
         self.matvecs = sum(len(c[2]) for c in self.calls)
 
     def __call__(self):

@@ -203,9 +203,11 @@ int qmv_matvec_grouped(int fmt, int64_t K, int64_t batch, int count, const qmv_m
   }
   if ((st = check_device())) return st;
   hipStream_t s = as_stream(stream);
-  if (batch == 1) {
+  {
     hipError_t e = hipSuccess;
-    if (qmv::launch_matvec_grouped_b1(fmt, K, count, items, x_dtype, s, &e)) return launched(e, "grouped matvec");
+    if (batch == 1 ? qmv::launch_matvec_grouped_b1(fmt, K, count, items, x_dtype, s, &e)
+                   : qmv::launch_matvec_grouped_mfma(fmt, K, batch, count, items, x_dtype, s, &e))
+      return launched(e, "grouped matvec");
   }
   for (int i = 0; i < count; ++i) {
     const hipError_t e = qmv::launch_matvec(fmt, items[i].N, K, batch, static_cast<const uint8_t*>(items[i].W),

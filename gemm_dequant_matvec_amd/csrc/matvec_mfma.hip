@@ -28,6 +28,7 @@
 // D[i][j] in lane j + 16 * (i / 4), element i % 4.  Any permutation of the k
 // of one MFMA that A and B share leaves the product unchanged; the loaders
 // below pick the one that makes each lane's weight bytes contiguous.
+#include <algorithm>
 #include <cstdlib>
 
 #include "qmv_internal.h"
@@ -50,6 +51,25 @@ struct MfmaArgs {
   const void* x;             // [nv][K]
   float* y;                  // [nv][N]
   int N, K, nv, waves;
+};
+
+// Up to kMaxSeg matrices of one format, K and vector count per launch (a
+// grouped call): each segment owns a contiguous range of workgroups, sized in
+// proportion to its 16-row tiles; a workgroup finds its segment once, builds
+// that segment's activation operands and strides over its tiles only.  The
+// table travels in the kernel arguments.
+constexpr int kMaxSeg = 16;
+struct MSeg {
+  const uint8_t* W;
+  int64_t off1, off2, off3;
+  const void* x;
+  float* y;
+  int N;
+  int b0, nb;  // first workgroup, workgroups
+};
+struct MTable {
+  MSeg s[kMaxSeg];
+  int count, K, nv, waves;
 };
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -345,7 +365,12 @@ struct Staging {
 //               k = 32u + 16s + 8(G/2) + 2e + G%2  (e = 0..3: one byte lane of one 6-bit code
 //                                                  word; elements 4s + e of the A fragment)
 template <int FMT, bool XF16, int KF>
-__global__ __launch_bounds__(64 * kMaxWaves) void matvec_mfma_kernel(const MfmaArgs a) {
+__global__ __launch_bounds__(64 * kMaxWaves) void matvec_mfma_kernel(const MTable tb) {
+  int si = 0;  // this workgroup's segment (workgroup-uniform scan)
+  for (int i = 1; i < tb.count; ++i) si = (int(blockIdx.x) >= tb.s[i].b0) ? i : si;
+  const MSeg& sg = tb.s[si];
+  const MfmaArgs a{sg.W, sg.off1, sg.off2, sg.off3, sg.x, sg.y, sg.N, tb.K, tb.nv, tb.waves};
+  const int bid = int(blockIdx.x) - sg.b0, nblk = sg.nb;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: chunk bases in SGPRs
   const int G = lane >> 4;
@@ -366,7 +391,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void matvec_mfma_kernel(const MfmaA
   float* red = reinterpret_cast<float*>(red_raw);
 
   // first chunk of the first tile in flight before the activations are set up
-  int tile = blockIdx.x;  // < ntiles (grid <= ntiles)
+  int tile = bid;  // < ntiles (a segment has at most as many workgroups as tiles)
   Stage<FMT> R = stg.load(tile, u0);
 
   // ---- A operands of this wave's K slice, built once (zero past K and for
@@ -410,7 +435,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void matvec_mfma_kernel(const MfmaA
       const Stage<FMT> cur = R;
       // next chunk: the following one of this tile, else the first of the next tile
       if (c + 1 < nch) R = stg.load(tile, u0 + 8 * (c + 1));
-      else if (tile + int(gridDim.x) < ntiles) R = stg.load(tile + gridDim.x, u0);
+      else if (tile + nblk < ntiles) R = stg.load(tile + nblk, u0);
       stg.compute(cur, lds, A + 8 * c, u0 + 8 * c, acc0, acc1);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // operand reads done before the next store
     }
@@ -430,7 +455,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void matvec_mfma_kernel(const MfmaA
       if (v < a.nv && r < N) a.y[int64_t(v) * N + r] = s;
     }
     buf ^= 1;
-    tile += gridDim.x;
+    tile += nblk;
     if (tile >= ntiles) break;
   }
 }
@@ -443,26 +468,56 @@ int blocks_override() {
   return v;
 }
 
+// Workgroups: up to 512 per launch (tuning override above), split over the
+// segments in proportion to their tiles, at least one and at most one per tile.
 template <int FMT, bool XF16, int KF>
-hipError_t go(const MfmaArgs& a, hipStream_t s) {
-  const int ntiles = (a.N + 15) / 16;
-  int blocks = blocks_override();
-  if (blocks <= 0) blocks = 512;
-  if (blocks > ntiles) blocks = ntiles;
-  hipLaunchKernelGGL((matvec_mfma_kernel<FMT, XF16, KF>), dim3(blocks), dim3(64 * a.waves), 0, s, a);
+hipError_t go(MTable& t, hipStream_t s) {
+  int64_t tiles[kMaxSeg], total = 0;
+  for (int i = 0; i < t.count; ++i) {
+    tiles[i] = (t.s[i].N + 15) / 16;
+    total += tiles[i];
+  }
+  int64_t budget = blocks_override();
+  if (budget <= 0) budget = 512;
+  if (budget > total) budget = total;
+  int b = 0;
+  for (int i = 0; i < t.count; ++i) {
+    const int64_t share = (budget * tiles[i] + total - 1) / total;
+    t.s[i].b0 = b;
+    t.s[i].nb = int(std::max<int64_t>(1, std::min(tiles[i], share)));
+    b += t.s[i].nb;
+  }
+  hipLaunchKernelGGL((matvec_mfma_kernel<FMT, XF16, KF>), dim3(b), dim3(64 * t.waves), 0, s, t);
   return hipGetLastError();
 }
 
 template <int FMT, bool XF16>
-bool pick_kf(MfmaArgs& a, hipStream_t s, hipError_t* err) {
-  const int U = a.K / 32;
+bool pick_kf(MTable& t, hipStream_t s, hipError_t* err) {
+  const int U = t.K / 32;
   // fragments per wave, a multiple of 8 (whole Q4K / Q6K super-blocks, W4A16
   // group pairs): 8 up to K = 2048, else 24 (K <= 6144), at most 8 waves
   const int kf = U <= 8 * kMaxWaves ? 8 : 24;
-  a.waves = (U + kf - 1) / kf;
-  if (a.waves > kMaxWaves) return false;
-  *err = kf == 8 ? go<FMT, XF16, 8>(a, s) : go<FMT, XF16, 24>(a, s);
+  t.waves = (U + kf - 1) / kf;
+  if (t.waves > kMaxWaves) return false;
+  *err = kf == 8 ? go<FMT, XF16, 8>(t, s) : go<FMT, XF16, 24>(t, s);
   return true;
+}
+
+bool launch_table(int fmt, MTable& t, int x_dtype, hipStream_t s, hipError_t* err) {
+  const bool f16 = (x_dtype == QMV_F16);
+  switch (fmt) {
+    case QMV_Q8_0: return pick_kf<QMV_Q8_0, false>(t, s, err);
+    case QMV_W4A16_G64:
+      return f16 ? pick_kf<QMV_W4A16_G64, true>(t, s, err) : pick_kf<QMV_W4A16_G64, false>(t, s, err);
+    case QMV_Q4K: return pick_kf<QMV_Q4K, false>(t, s, err);
+    case QMV_Q6K: return pick_kf<QMV_Q6K, false>(t, s, err);
+    default: return false;
+  }
+}
+
+bool fits(int fmt, int64_t N, int64_t K) {
+  // the kernel addresses planes with 32-bit offsets; K up to 8 waves x 24 blocks
+  return planes_of(fmt, N, K).total < (int64_t(1) << 31) && K / 32 <= 8 * 24;
 }
 
 }  // namespace
@@ -471,18 +526,43 @@ bool pick_kf(MfmaArgs& a, hipStream_t s, hipError_t* err) {
 // shapes outside this kernel's range (K > 6144, packed matrix >= 2 GiB).
 bool launch_matvec_mfma(int fmt, int64_t N, int64_t K, int nv, const uint8_t* W, const void* x, int x_dtype,
                         float* y, hipStream_t s, hipError_t* err) {
+  if (!fits(fmt, N, K)) return false;
   const Planes p = planes_of(fmt, N, K);
-  if (p.total >= (int64_t(1) << 31)) return false;  // the kernel addresses planes with 32-bit offsets
-  MfmaArgs a{W, p.off[1], p.off[2], p.off[3], x, y, int(N), int(K), nv, 0};
-  const bool f16 = (x_dtype == QMV_F16);
-  switch (fmt) {
-    case QMV_Q8_0: return pick_kf<QMV_Q8_0, false>(a, s, err);
-    case QMV_W4A16_G64:
-      return f16 ? pick_kf<QMV_W4A16_G64, true>(a, s, err) : pick_kf<QMV_W4A16_G64, false>(a, s, err);
-    case QMV_Q4K: return pick_kf<QMV_Q4K, false>(a, s, err);
-    case QMV_Q6K: return pick_kf<QMV_Q6K, false>(a, s, err);
-    default: return false;
+  MTable t{};
+  t.count = 1;
+  t.K = int(K);
+  t.nv = nv;
+  t.s[0] = MSeg{W, p.off[1], p.off[2], p.off[3], x, y, int(N), 0, 0};
+  return launch_table(fmt, t, x_dtype, s, err);
+}
+
+// Several matvecs of one format, K and batch (>= 2) on the matrix cores: per
+// chunk of up to 8 vectors, one launch per kMaxSeg items.  Returns false
+// (nothing launched) when some item is outside the kernel's range.
+bool launch_matvec_grouped_mfma(int fmt, int64_t K, int64_t batch, int count, const qmv_matvec_item* items,
+                                int x_dtype, hipStream_t s, hipError_t* err) {
+  for (int i = 0; i < count; ++i)
+    if (!fits(fmt, items[i].N, K)) return false;
+  const int64_t xel = (x_dtype == QMV_F16) ? 2 : 4;
+  for (int64_t b0 = 0; b0 < batch; b0 += 8) {
+    const int nv = int(batch - b0 < 8 ? batch - b0 : 8);
+    for (int i0 = 0; i0 < count; i0 += kMaxSeg) {
+      MTable t{};
+      t.K = int(K);
+      t.nv = nv;
+      t.count = count - i0 < kMaxSeg ? count - i0 : kMaxSeg;
+      for (int i = 0; i < t.count; ++i) {
+        const qmv_matvec_item& it = items[i0 + i];
+        const Planes p = planes_of(fmt, it.N, K);
+        t.s[i] = MSeg{static_cast<const uint8_t*>(it.W), p.off[1], p.off[2], p.off[3],
+                      static_cast<const uint8_t*>(it.x) + b0 * K * xel, static_cast<float*>(it.y) + b0 * it.N,
+                      int(it.N), 0, 0};
+      }
+      if (!launch_table(fmt, t, x_dtype, s, err)) return false;
+      if (*err != hipSuccess) return true;
+    }
   }
+  return true;
 }
 
 }  // namespace qmv

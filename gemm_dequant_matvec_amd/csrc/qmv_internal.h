@@ -85,6 +85,8 @@ bool launch_matvec_b1(int fmt, int64_t N, int64_t K, const uint8_t* W, const voi
                       float* y, hipStream_t s, hipError_t* err);
 bool launch_matvec_mfma(int fmt, int64_t N, int64_t K, int nv, const uint8_t* W, const void* x, int x_dtype,
                         float* y, hipStream_t s, hipError_t* err);
+bool launch_matvec_grouped_mfma(int fmt, int64_t K, int64_t batch, int count, const qmv_matvec_item* items,
+                                int x_dtype, hipStream_t s, hipError_t* err);
 bool launch_matvec_grouped_b1(int fmt, int64_t K, int count, const qmv_matvec_item* items, int x_dtype,
                               hipStream_t s, hipError_t* err);
 hipError_t launch_gemm(int fmt, int64_t N, int64_t K, int64_t M, const uint8_t* W,

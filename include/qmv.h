@@ -173,11 +173,13 @@ int qmv_matvec(int fmt, int64_t N, int64_t K, int64_t batch, const void* W,
  * possible: for every item i, y_i[b][n] = sum_k W_i[n][k] * x_i[b][k].
  * The grouped dispatch of the pages' decoders: the q / k / v projections in
  * one dispatch with the simdgroups spread over the three matrices, gate / up
- * in another (aot-llm README, Metal backend notes).  At batch 1, up to 16
- * items share one launch (their row groups are laid end to end and each wave
- * reloads x only when it moves to an item with other activations); other
- * batches run one qmv_matvec launch per item.  Dtypes and alignment as
- * qmv_matvec; count >= 1.
+ * in another (aot-llm README, Metal backend notes).  Up to 16 items share
+ * one launch (per chunk of 8 vectors at batch >= 2); the launch's workgroups
+ * are split over the items in proportion to their rows.  Items outside the
+ * grouped kernels' range (K above 6144 at batch >= 2, or an activation slice
+ * too wide for registers at batch 1) run one qmv_matvec launch each.  Each
+ * item's result equals its qmv_matvec result bit for bit.  Dtypes and
+ * alignment as qmv_matvec; count >= 1.
  * Errors: FORMAT, SHAPE, NULL, ALIGN, DTYPE, UNSUPPORTED, OVERFLOW, DEVICE, LAUNCH
  * (the message names the offending item).
  */

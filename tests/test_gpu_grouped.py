@@ -102,9 +102,31 @@ def test_grouped_equals_single_calls_bitwise(qmv, fmt):
         assert torch.equal(single.view(torch.int32), y.view(torch.int32))
 
 
-@pytest.mark.parametrize("batch", [2, 8])
-def test_grouped_batched_runs_per_item(qmv, batch):
-    _run_and_check(qmv, "q4k", [300, 17], 1024, batch, "f32", True, seed=5)
+@pytest.mark.parametrize("fmt", wl.FORMATS)
+@pytest.mark.parametrize("batch", [2, 8, 11])
+@pytest.mark.parametrize("shared_x", [True, False])
+def test_grouped_batched_parity(qmv, fmt, batch, shared_x):
+    # batch >= 2: the matrix-core kernel, items laid side by side (11: two chunks)
+    K = wl.BLOCK[fmt] * 8
+    _run_and_check(qmv, fmt, [300, 17, 1, 129], K, batch, XDT[fmt], shared_x, seed=5)
+
+
+def test_grouped_batched_many_items_and_wide_k(qmv):
+    shapes = [int(n) for n in np.random.default_rng(8).integers(1, 90, 19)]
+    _run_and_check(qmv, "q6k", shapes, 2048, 8, "f32", False, seed=8)
+    # K past the matrix-core kernel's range: one launch per item
+    _run_and_check(qmv, "q4k", [40, 9], 6400, 8, "f32", True, seed=9)
+
+
+@pytest.mark.parametrize("fmt", ["q4k", "q6k", "w4a16_g64"])
+def test_grouped_batched_equals_single_calls_bitwise(qmv, fmt):
+    K = wl.BLOCK[fmt] * 16 if fmt != "w4a16_g64" else 4096
+    shapes = [700, 64, 2049]
+    ws, Wps, xd, items, ys = _run_and_check(qmv, fmt, shapes, K, 8, XDT[fmt], True, seed=10)
+    for (Wp, x, N), y in zip(items, ys):
+        single = qmv.matvec(fmt, Wp, x, N, K)
+        torch.cuda.synchronize()
+        assert torch.equal(single.view(torch.int32), y.view(torch.int32))
 
 
 def test_grouped_wide_k_falls_back(qmv):
