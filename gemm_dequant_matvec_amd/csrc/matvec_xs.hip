@@ -405,18 +405,18 @@ hipError_t go(SegTable& t, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Rows per lane group, from measurements on MI355X (W4A16 / Q4K / Q6K, K = 1024
-// to 5632): two rows once a launch streams 2 MB or more (twice the loads in
-// flight per wave and half the activation reloads outweigh the waves lost),
-// four once every wave slot of the chip (4096) would walk 16 rows or more,
-// one row below 2 MB, where the launch is latency-bound and waves count.
+// Rows per lane group, from measurements on MI355X over twelve shapes (all
+// formats, K = 512 to 5632, 256 to 151936 rows, R = 1, 2, 4): one row when the
+// launch has at most 1024 row slots (rows / rows read side by side per wave:
+// the launch is latency-bound and waves count), else two (twice the loads in
+// flight per wave, half the activation reloads), four for Q6K from 16384 slots
+// (the 32000 x 2048 head: 5 % faster than two).
 template <int FMT, bool XF16, int LPR, int UPL>
 hipError_t pick_r(SegTable& t, int rsel, hipStream_t s) {
   int64_t rows = 0;
   for (int i = 0; i < t.count; ++i) rows += t.s[i].N;
-  const int64_t weight_bytes = rows * int64_t(t.K) * (FMT == QMV_Q8_0 ? 34 : FMT == QMV_Q6K ? 26 : 18) / 32;
-  const int64_t rows_per_slot = rows / (64 / LPR) / 4096;
-  const int r = rsel ? rsel : rows_per_slot >= 16 ? 4 : weight_bytes >= (int64_t(2) << 20) ? 2 : 1;
+  const int64_t slots = rows / (64 / LPR);
+  const int r = rsel ? rsel : slots <= 1024 ? 1 : (FMT == QMV_Q6K && slots >= 16384) ? 4 : 2;
   if (r == 4) return go<FMT, XF16, LPR, UPL, 4>(t, s);
   return r == 2 ? go<FMT, XF16, LPR, UPL, 2>(t, s) : go<FMT, XF16, LPR, UPL, 1>(t, s);
 }
@@ -425,7 +425,13 @@ template <int FMT, bool XF16>
 bool dispatch(SegTable& t, int rsel, hipStream_t s, hipError_t* e) {
   constexpr bool H2 = (FMT == QMV_W4A16_G64 && XF16);
   const int U = t.K / 32;
-  const int lpr = U >= 64 ? 64 : (U > 16 ? 32 : 16);
+  static const int lpr_forced = [] {  // A/B tuning only: lanes per row (16, 32 or 64)
+    const char* e = getenv("QMV_MATVEC_LPR");
+    const int v = e ? atoi(e) : 0;
+    return (v == 16 || v == 32 || v == 64) ? v : 0;
+  }();
+  int lpr = U >= 64 ? 64 : (U > 16 ? 32 : 16);
+  if (lpr_forced && lpr_forced < lpr && (U + lpr_forced - 1) / lpr_forced <= 2) lpr = lpr_forced;
   const int upl = (U + lpr - 1) / lpr;
   // activation registers per unit: 17 (fp16 pairs) or 34 (f32)
   if (upl > (H2 ? 4 : 3)) return false;
@@ -443,7 +449,7 @@ bool dispatch(SegTable& t, int rsel, hipStream_t s, hipError_t* e) {
     *e = upl == 1 ? pick_r<FMT, XF16, 32, 1>(t, rsel, s) : pick_r<FMT, XF16, 32, 2>(t, rsel, s);
     return true;
   }
-  *e = pick_r<FMT, XF16, 16, 1>(t, rsel, s);
+  *e = upl == 1 ? pick_r<FMT, XF16, 16, 1>(t, rsel, s) : pick_r<FMT, XF16, 16, 2>(t, rsel, s);
   return true;
 }
 
