@@ -23,7 +23,8 @@ M = 16 / 128 / 512 in TFLOP/s), a plain-copy bandwidth probe, and the CPU
 oracle timed on the host (`cpu_baseline`).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--copies C]
-                       [--no-extras] [--no-cpu-baseline]
+                       [--no-extras] [--no-cpu-baseline] [--leg NAME]
+(--leg runs one extras workload alone and prints its result, for profiling.)
 """
 from __future__ import annotations
 
@@ -56,6 +57,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
+    p.add_argument("--leg", default=None,
+                   help="run only this extras workload and print its result (profiling); one of: "
+                        + ", ".join(LEGS))
     return p.parse_args()
 
 
@@ -269,47 +273,63 @@ def copy_probe():
     return {"bytes": 2 * n, "gbs": 2 * n / (ms * 1e-3) / 1e9, "what": "torch copy_ of 1 GiB (read+write)"}
 
 
-def extras(qmv, args):
+def leg_q8_0(qmv):
+    """Q8_0 512x512: one launch, latency-bound (same matrix 20x back to back)."""
     import workloads as wl
-    res = {}
-    # Q8_0 512x512: one launch, latency-bound
-    c1 = wl.c1_q8_0()
-    st = Stream(qmv, c1["mats"], "f32", 1, 1)
+    st = Stream(qmv, wl.c1_q8_0()["mats"], "f32", 1, 1)
     ms, _ = time_graph(lambda: [st() for _ in range(20)], 20, 5)
     ms /= 20
-    res["q8_0_512x512_b1_single"] = {"us": ms * 1e3, "gbs": st.bytes / (ms * 1e-3) / 1e9,
-                                     "note": "same matrix 20x back to back (cache-warm)"}
-    del st
-    # Q4K 0.6B MLP (cold, 170 copies of each = 608 MB) and the vocab head (8 copies = 705 MB)
-    c3 = wl.c3_q4k_0b6()
-    mlp = [m for m in c3["mats"] if m[0] != "head"]
+    return {"us": ms * 1e3, "gbs": st.bytes / (ms * 1e-3) / 1e9,
+            "note": "same matrix 20x back to back (cache-warm)"}
+
+
+def leg_mlp06(qmv):
+    """Q4K 0.6B MLP up / down, 170 cold copies of each (608 MB)."""
+    import workloads as wl
+    mlp = [m for m in wl.c3_q4k_0b6()["mats"] if m[0] != "head"]
     st = Stream(qmv, mlp, "f32", 1, 170)
     ms, _ = time_graph(st, 10, 3)
-    res["q4k_0.6B_mlp_b1_cold"] = {"us_per_launch": ms * 1e3 / st.launches,
-                                   "gbs": st.bytes / (ms * 1e-3) / 1e9, "launches": st.launches}
-    del st
-    head = [m for m in c3["mats"] if m[0] == "head"]
+    return {"us_per_launch": ms * 1e3 / st.launches, "gbs": st.bytes / (ms * 1e-3) / 1e9,
+            "launches": st.launches}
+
+
+def leg_head06(qmv):
+    """The 151936 x 1024 Q4K vocab head, 8 cold copies (705 MB)."""
+    import workloads as wl
+    head = [m for m in wl.c3_q4k_0b6()["mats"] if m[0] == "head"]
     st = Stream(qmv, head, "f32", 1, 8)
     ms, _ = time_graph(st, 10, 3)
-    res["q4k_vocab_head_151936x1024_b1_cold"] = {"us_per_launch": ms * 1e3 / st.launches,
-                                                 "gbs": st.bytes / (ms * 1e-3) / 1e9}
-    del st
-    # full decode sweep of the 1.1B decoder, batch 1 and 8 (155 matvecs, 667 MB of weights)
-    for b in (1, 8):
-        c5 = wl.c5_sweep(b)
-        st = Sweep(qmv, c5, b)
-        ms, _ = time_graph(st, 10, 3)
-        res[f"decode_sweep_1.1B_b{b}"] = {
-            "ms_per_token_step": ms, "tok_per_s": b / (ms * 1e-3),
-            "gbs": st.bytes / (ms * 1e-3) / 1e9, "bytes": st.bytes, "launches": st.launches,
-            "matvecs": st.matvecs}
-        del st
-    # prefill GEMM
-    for M in (16, 128, 512):
+    return {"us_per_launch": ms * 1e3 / st.launches, "gbs": st.bytes / (ms * 1e-3) / 1e9}
+
+
+def leg_sweep(qmv, b):
+    """One decode token of the 1.1B decoder at batch b: 155 matvecs, 667 MB of weights."""
+    import workloads as wl
+    st = Sweep(qmv, wl.c5_sweep(b), b)
+    ms, _ = time_graph(st, 10, 3)
+    return {"ms_per_token_step": ms, "tok_per_s": b / (ms * 1e-3), "gbs": st.bytes / (ms * 1e-3) / 1e9,
+            "bytes": st.bytes, "launches": st.launches, "matvecs": st.matvecs}
+
+
+LEGS = {
+    "q8_0_512x512_b1_single": leg_q8_0,
+    "q4k_0.6B_mlp_b1_cold": leg_mlp06,
+    "q4k_vocab_head_151936x1024_b1_cold": leg_head06,
+    "decode_sweep_1.1B_b1": lambda q: leg_sweep(q, 1),
+    "decode_sweep_1.1B_b8": lambda q: leg_sweep(q, 8),
+    "gemm_w4a16_M16": lambda q: gemm_leg(q, 16),
+    "gemm_w4a16_M128": lambda q: gemm_leg(q, 128),
+    "gemm_w4a16_M512": lambda q: gemm_leg(q, 512),
+}
+
+
+def extras(qmv, args):
+    res = {}
+    for name, fn in LEGS.items():
         try:
-            res[f"gemm_w4a16_M{M}"] = gemm_leg(qmv, M)
-        except Exception as e:  # GEMM not available: report, do not fake
-            res[f"gemm_w4a16_M{M}"] = {"error": str(e)[:200]}
+            res[name] = fn(qmv)
+        except Exception as e:  # a leg that cannot run is reported, not faked
+            res[name] = {"error": str(e)[:200]}
     return res
 
 
@@ -445,6 +465,12 @@ def main():
     import gemm_dequant_matvec_amd as qmv
     assert torch.cuda.is_available(), "no GPU visible"
     torch.cuda.set_device(0)
+    if args.leg is not None:
+        if args.leg not in LEGS:
+            print(f"unknown leg {args.leg!r}; one of {', '.join(LEGS)}", file=sys.stderr)
+            sys.exit(2)
+        print(json.dumps({"leg": args.leg, "result": LEGS[args.leg](qmv)}), flush=True)
+        return
 
     log("headline: W4A16 g64 1.1B MLP matvecs, batch 1, copies", args.copies)
     st, ms, gbs = headline(qmv, args)
