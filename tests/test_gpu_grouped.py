@@ -195,3 +195,35 @@ def test_config_decode_layer_qkv_grouped(qmv):
                                 oracle.tolerance_bound(W32, xv, TAU["matvec"]))
         _say(nm, r)
         assert r["ok"], (nm, r)
+
+
+@pytest.mark.parametrize("batch", [1, 8])
+def test_decode_sweep_launch_configuration(qmv, batch):
+    # the timed decode sweep's own launches (q + k and gate + up grouped), one
+    # 1.1B decoder layer plus the 32000-row head, against the oracle
+    import bench
+    cfg = wl.c5_sweep(batch, layers=1)
+    st = bench.Sweep(qmv, cfg, batch)
+    st()
+    torch.cuda.synchronize()
+    # weights and activations as the sweep draws them: one weight set per
+    # distinct shape (later matrices of that shape get copies of it), one vector
+    # set per shared input, each seeded with the key of the first matrix
+    first_key, shape_key = {}, {}
+    outs = [it[3] for _, _, items in st.calls for it in items]
+    assert len(outs) == len(cfg["mats"])
+    for (name, fmt, N, K, key), y in zip(cfg["mats"], outs):
+        layer, nm = name.split(".") if "." in name else ("", name)
+        share = (layer, bench.Sweep.SHARED.get(nm, nm))
+        first_key.setdefault(share, key)
+        shape_key.setdefault((fmt, N, K), key)
+        x = wl.gen_x(K, batch, "f32", first_key[share])
+        w = wl.gen_weights(fmt, N, K, shape_key[(fmt, N, K)])
+        rows = np.arange(N) if N <= 6000 else np.unique(
+            np.concatenate([[0, N - 1], np.random.default_rng(1).integers(0, N, 400)]))
+        W32 = oracle.dequant_rows(fmt, w, rows)
+        xv = x.astype(np.float64)
+        r = oracle.check_within(y.cpu().numpy()[:, rows], oracle.matvec_ref(W32, xv),
+                                oracle.tolerance_bound(W32, xv, TAU["matvec"]))
+        _say(name, batch, r)
+        assert r["ok"], (name, batch, r)
