@@ -43,7 +43,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kMaxWaves = 8;
+// waves per workgroup: up to 8 with 8 blocks of K per wave, up to 12 with 16
+template <int KF>
+constexpr int kMaxWaves = KF == 8 ? 8 : 12;
 
 struct MfmaArgs {
   const uint8_t* W;
@@ -365,7 +367,8 @@ struct Staging {
 //               k = 32u + 16s + 8(G/2) + 2e + G%2  (e = 0..3: one byte lane of one 6-bit code
 //                                                  word; elements 4s + e of the A fragment)
 template <int FMT, bool XF16, int KF>
-__global__ __launch_bounds__(64 * kMaxWaves) void matvec_mfma_kernel(const MTable tb) {
+__global__ __launch_bounds__(64 * kMaxWaves<KF>) void matvec_mfma_kernel(const MTable tb) {
+  constexpr int MW = kMaxWaves<KF>;
   int si = 0;  // this workgroup's segment (workgroup-uniform scan)
   for (int i = 1; i < tb.count; ++i) si = (int(blockIdx.x) >= tb.s[i].b0) ? i : si;
   const MSeg& sg = tb.s[si];
@@ -385,8 +388,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void matvec_mfma_kernel(const MTabl
   const int ntiles = (N + 15) >> 4;
   const Staging<FMT> stg{a, U, K >> 8, lane};
 
-  __shared__ uint32_t stage_lds[kMaxWaves][kStageDw<FMT>];
-  __shared__ f32x4 red_raw[2][kMaxWaves][32];  // [buffer][wave][lane pair] -> 2 x float2
+  __shared__ uint32_t stage_lds[MW][kStageDw<FMT>];
+  __shared__ f32x4 red_raw[2][MW][32];  // [buffer][wave][lane pair] -> 2 x float2
   uint32_t* lds = stage_lds[wave];
   float* red = reinterpret_cast<float*>(red_raw);
 
@@ -441,7 +444,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void matvec_mfma_kernel(const MTabl
     }
 
     // ---- the W partial sums of this tile meet in LDS, added in wave order
-    float* rb = red + (buf * kMaxWaves + wave) * 128;
+    float* rb = red + (buf * MW + wave) * 128;
     rb[2 * lane] = acc0;
     rb[2 * lane + 1] = acc1;
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -450,7 +453,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void matvec_mfma_kernel(const MTabl
       const int v = t >> 4;  // vector
       const int src = 2 * (i + 16 * (v >> 1)) + (v & 1);
       float s = 0.0f;
-      for (int w = 0; w < a.waves; ++w) s += red[(buf * kMaxWaves + w) * 128 + src];
+      for (int w = 0; w < a.waves; ++w) s += red[(buf * MW + w) * 128 + src];
       const int r = tile * 16 + i;
       if (v < a.nv && r < N) a.y[int64_t(v) * N + r] = s;
     }
@@ -495,11 +498,12 @@ template <int FMT, bool XF16>
 bool pick_kf(MTable& t, hipStream_t s, hipError_t* err) {
   const int U = t.K / 32;
   // fragments per wave, a multiple of 8 (whole Q4K / Q6K super-blocks, W4A16
-  // group pairs): 8 up to K = 2048, else 24 (K <= 6144), at most 8 waves
-  const int kf = U <= 8 * kMaxWaves ? 8 : 24;
+  // group pairs): 8 up to K = 2048 (at most 8 waves), else 16 (at most 12 waves,
+  // K <= 6144)
+  const int kf = U <= 8 * kMaxWaves<8> ? 8 : 16;
   t.waves = (U + kf - 1) / kf;
-  if (t.waves > kMaxWaves) return false;
-  *err = kf == 8 ? go<FMT, XF16, 8>(t, s) : go<FMT, XF16, 24>(t, s);
+  if (t.waves > (kf == 8 ? kMaxWaves<8> : kMaxWaves<16>)) return false;
+  *err = kf == 8 ? go<FMT, XF16, 8>(t, s) : go<FMT, XF16, 16>(t, s);
   return true;
 }
 
@@ -516,8 +520,8 @@ bool launch_table(int fmt, MTable& t, int x_dtype, hipStream_t s, hipError_t* er
 }
 
 bool fits(int fmt, int64_t N, int64_t K) {
-  // the kernel addresses planes with 32-bit offsets; K up to 8 waves x 24 blocks
-  return planes_of(fmt, N, K).total < (int64_t(1) << 31) && K / 32 <= 8 * 24;
+  // the kernel addresses planes with 32-bit offsets; K up to 12 waves x 16 blocks
+  return planes_of(fmt, N, K).total < (int64_t(1) << 31) && K / 32 <= 12 * 16;
 }
 
 }  // namespace
