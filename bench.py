@@ -336,8 +336,9 @@ def extras(qmv, args):
 class Sweep:
     """The 155 matvecs of one decode token: distinct shapes generated once, every
     layer gets its own device copy (so the 667 MB sweep streams from HBM).
-    Matrices that read the same activations and share a format run as one
-    grouped call: q + k (Q4K), gate + up; v (Q6K), o, down and the head alone."""
+    Matrices that read the same activations and share a format (or are all
+    Q4K / Q6K) run as one grouped call: q + k (Q4K) + v (Q6K), gate + up; o,
+    down and the head alone."""
 
     SHARED = {"q": "attn_in", "k": "attn_in", "v": "attn_in", "gate": "mlp_in", "up": "mlp_in"}
 
@@ -346,7 +347,7 @@ class Sweep:
         import workloads as wl
         self.qmv, self.batch = qmv, batch
         shapes, xs = {}, {}
-        self.calls = []  # (fmt, K, [(W, x, N, y), ...])
+        self.calls = []  # (fmt or None when mixed, K, [(W, x, N, y, fmt), ...])
         prev = None
         self.bytes = 0
         for name, fmt, N, K, key in cfg["mats"]:
@@ -363,19 +364,21 @@ class Sweep:
                 self.bytes += batch * K * 4
             y = torch.empty((batch, N), dtype=torch.float32, device="cuda")
             self.bytes += int(round(wl.bytes_per_weight(fmt) * N * K)) + batch * N * 4
-            item = (W, xs[share], N, y)
-            if prev == (share, fmt, K):
-                self.calls[-1][2].append(item)
+            item = (W, xs[share], N, y, fmt)
+            fmts = {fmt} | ({it[4] for it in self.calls[-1][2]} if prev == (share, K) else set())
+            if prev == (share, K) and (len(fmts) == 1 or fmts <= {"q4k", "q6k"}):
+                _, _, items = self.calls[-1]
+                self.calls[-1] = (fmt if len(fmts) == 1 else None, K, items + [item])
             else:
                 self.calls.append((fmt, K, [item]))
-            prev = (share, fmt, K)
+            prev = (share, K)
         self.launches = len(self.calls)
         self.matvecs = sum(len(c[2]) for c in self.calls)
 
     def __call__(self):
         for fmt, K, items in self.calls:
             if len(items) == 1:
-                W, x, N, y = items[0]
+                W, x, N, y, _ = items[0]
                 self.qmv.matvec(fmt, W, x, N, K, y=y)
             else:
                 self.qmv.matvec_grouped(fmt, items, K)

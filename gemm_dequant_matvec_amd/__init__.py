@@ -59,7 +59,8 @@ _lib.qmv_matvec.restype = _int
 
 
 class QmvMatvecItem(ctypes.Structure):
-    _fields_ = [("N", ctypes.c_int64), ("W", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p)]
+    _fields_ = [("N", ctypes.c_int64), ("W", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("fmt", ctypes.c_int32)]
 
 
 _lib.qmv_matvec_grouped.argtypes = [_int, _i64, _i64, _int, ctypes.POINTER(QmvMatvecItem), _int, _int, _vp]
@@ -155,10 +156,12 @@ def matvec(fmt, W: torch.Tensor, x: torch.Tensor, N: int, K: int, y: torch.Tenso
 
 
 def matvec_grouped(fmt, items, K: int, stream=None) -> list:
-    """Several matvecs of one format and K in as few launches as possible.
+    """Several matvecs of one K in as few launches as possible.
 
-    items: sequence of (W, x, N) or (W, x, N, y); x [b][K] (same b and dtype for
-    all), y allocated as f32 [b][N] when absent.  Returns the list of y.
+    items: sequence of (W, x, N), (W, x, N, y) or (W, x, N, y, item_fmt); x
+    [b][K] (same b and dtype for all), y allocated as f32 [b][N] when absent or
+    None; item_fmt overrides fmt for that matrix (fmt may then be None).
+    Returns the list of y.
     """
     arr = (QmvMatvecItem * len(items))()
     outs = []
@@ -170,11 +173,13 @@ def matvec_grouped(fmt, items, K: int, stream=None) -> list:
             b, xdt = x2.shape[0], x2.dtype
         if x2.shape != (b, K) or x2.dtype != xdt:
             raise ValueError("all items need x of shape [b][K] and one dtype")
-        y = it[3] if len(it) > 3 else torch.empty((b, N), dtype=torch.float32, device=x.device)
+        y = it[3] if len(it) > 3 and it[3] is not None else torch.empty((b, N), dtype=torch.float32,
+                                                                          device=x.device)
         arr[i].N, arr[i].W, arr[i].x, arr[i].y = N, _ptr(W), _ptr(x2), _ptr(y)
+        arr[i].fmt = _fmt(it[4]) if len(it) > 4 and it[4] is not None else 0
         outs.append(y)
-    _check(_lib.qmv_matvec_grouped(_fmt(fmt), K, b, len(items), arr, _DTYPES[xdt], _DTYPES[torch.float32],
-                                   _stream(stream)))
+    _check(_lib.qmv_matvec_grouped(0 if fmt is None else _fmt(fmt), K, b, len(items), arr, _DTYPES[xdt],
+                                   _DTYPES[torch.float32], _stream(stream)))
     return outs
 
 

@@ -157,7 +157,14 @@ int qmv_pack(int fmt, int64_t N, int64_t K, int64_t batch, const qmv_logical* sr
 static int check_matvec_args(int fmt, int64_t N, int64_t K, int64_t batch, const void* W, const void* x,
                              int x_dtype, const void* y, int y_dtype, const char* who) {
   int st;
-  if ((st = check_shape(fmt, N, K, batch, "batch"))) return st;
+  if ((st = check_shape(fmt, N, K, batch, "batch"))) {
+    if (*who) {  // name the item
+      char msg[sizeof(g_last_error)];
+      std::snprintf(msg, sizeof(msg), "%s", g_last_error);
+      fail(st, "%s%s", who, msg);
+    }
+    return st;
+  }
   if (!W) return fail(QMV_ERR_NULL, "%sW is NULL", who);
   if (!x) return fail(QMV_ERR_NULL, "%sx is NULL", who);
   if (!y) return fail(QMV_ERR_NULL, "%sy is NULL", who);
@@ -166,7 +173,7 @@ static int check_matvec_args(int fmt, int64_t N, int64_t K, int64_t batch, const
   if (y_dtype != QMV_F32 && y_dtype != QMV_F16 && y_dtype != QMV_BF16)
     return fail(QMV_ERR_DTYPE, "y_dtype=%d is not a qmv_dtype", y_dtype);
   if (x_dtype == QMV_BF16 || (x_dtype == QMV_F16 && fmt != QMV_W4A16_G64))
-    return fail(QMV_ERR_UNSUPPORTED, "%s matvec takes x as f32%s", fmt_name(fmt),
+    return fail(QMV_ERR_UNSUPPORTED, "%s%s matvec takes x as f32%s", who, fmt_name(fmt),
                 fmt == QMV_W4A16_G64 ? " or f16" : "");
   if (y_dtype != QMV_F32) return fail(QMV_ERR_UNSUPPORTED, "matvec writes y as f32 only");
   if (!aligned(W, 16)) return fail(QMV_ERR_ALIGN, "%sW is not 16-byte aligned", who);
@@ -191,13 +198,16 @@ int qmv_matvec(int fmt, int64_t N, int64_t K, int64_t batch, const void* W, cons
 int qmv_matvec_grouped(int fmt, int64_t K, int64_t batch, int count, const qmv_matvec_item* items,
                        int x_dtype, int y_dtype, void* stream) {
   int st;
-  if ((st = check_fmt(fmt))) return st;
-  if (count < 1) return fail(QMV_ERR_SHAPE, "count=%d must be >= 1", count);
+  if (fmt != 0 && (st = check_fmt(fmt))) return st;
+  if (count < 1 || count > 4096) return fail(QMV_ERR_SHAPE, "count=%d must be in [1, 4096]", count);
   if (!items) return fail(QMV_ERR_NULL, "items is NULL");
   char who[32];
   for (int i = 0; i < count; ++i) {
     std::snprintf(who, sizeof(who), "items[%d].", i);
-    if ((st = check_matvec_args(fmt, items[i].N, K, batch, items[i].W, items[i].x, x_dtype, items[i].y,
+    const int f = items[i].fmt ? items[i].fmt : fmt;
+    if (f == 0) return fail(QMV_ERR_FORMAT, "%sfmt is 0 and the call's fmt is 0", who);
+    if (qmv::block_of(f) == 0) return fail(QMV_ERR_FORMAT, "%sfmt=%d is not a qmv_format", who, f);
+    if ((st = check_matvec_args(f, items[i].N, K, batch, items[i].W, items[i].x, x_dtype, items[i].y,
                                 y_dtype, who)))
       return st;
   }
@@ -210,7 +220,8 @@ int qmv_matvec_grouped(int fmt, int64_t K, int64_t batch, int count, const qmv_m
       return launched(e, "grouped matvec");
   }
   for (int i = 0; i < count; ++i) {
-    const hipError_t e = qmv::launch_matvec(fmt, items[i].N, K, batch, static_cast<const uint8_t*>(items[i].W),
+    const int f = items[i].fmt ? items[i].fmt : fmt;
+    const hipError_t e = qmv::launch_matvec(f, items[i].N, K, batch, static_cast<const uint8_t*>(items[i].W),
                                             items[i].x, x_dtype, static_cast<float*>(items[i].y), s);
     if (e != hipSuccess) return launched(e, "grouped matvec");
   }

@@ -68,7 +68,9 @@ struct MSeg {
   float* y;
   int N;
   int b0, nb;  // first workgroup, workgroups
+  int fmt;     // format (read by the mixed Q4K / Q6K kernel only)
 };
+constexpr int kMixM = 0;  // table format of a Q4K / Q6K mix
 struct MTable {
   MSeg s[kMaxSeg];
   int count, K, nv, waves;
@@ -366,12 +368,12 @@ struct Staging {
 //   Q6K         two 16x16x16 MFMAs, sub-block s = 0, 1:
 //               k = 32u + 16s + 8(G/2) + 2e + G%2  (e = 0..3: one byte lane of one 6-bit code
 //                                                  word; elements 4s + e of the A fragment)
-template <int FMT, bool XF16, int KF>
-__global__ __launch_bounds__(64 * kMaxWaves<KF>) void matvec_mfma_kernel(const MTable tb) {
+//
+// One workgroup's share of one segment: stage is the workgroup's staging LDS
+// (SD dwords per wave), red its reduction LDS.
+template <int FMT, bool XF16, int KF, int SD>
+__device__ __forceinline__ void mfma_segment(const MTable& tb, const MSeg& sg, uint32_t* stage, float* red) {
   constexpr int MW = kMaxWaves<KF>;
-  int si = 0;  // this workgroup's segment (workgroup-uniform scan)
-  for (int i = 1; i < tb.count; ++i) si = (int(blockIdx.x) >= tb.s[i].b0) ? i : si;
-  const MSeg& sg = tb.s[si];
   const MfmaArgs a{sg.W, sg.off1, sg.off2, sg.off3, sg.x, sg.y, sg.N, tb.K, tb.nv, tb.waves};
   const int bid = int(blockIdx.x) - sg.b0, nblk = sg.nb;
   const int lane = threadIdx.x & 63;
@@ -388,10 +390,7 @@ __global__ __launch_bounds__(64 * kMaxWaves<KF>) void matvec_mfma_kernel(const M
   const int ntiles = (N + 15) >> 4;
   const Staging<FMT> stg{a, U, K >> 8, lane};
 
-  __shared__ uint32_t stage_lds[MW][kStageDw<FMT>];
-  __shared__ f32x4 red_raw[2][MW][32];  // [buffer][wave][lane pair] -> 2 x float2
-  uint32_t* lds = stage_lds[wave];
-  float* red = reinterpret_cast<float*>(red_raw);
+  uint32_t* lds = stage + wave * SD;
 
   // first chunk of the first tile in flight before the activations are set up
   int tile = bid;  // < ntiles (a segment has at most as many workgroups as tiles)
@@ -463,6 +462,27 @@ __global__ __launch_bounds__(64 * kMaxWaves<KF>) void matvec_mfma_kernel(const M
   }
 }
 
+// FMT = kMixM: a table of Q4K and Q6K segments, each workgroup taking its
+// segment's format path (a workgroup-uniform branch).
+template <int FMT, bool XF16, int KF>
+__global__ __launch_bounds__(64 * kMaxWaves<KF>) void matvec_mfma_kernel(const MTable tb) {
+  constexpr int MW = kMaxWaves<KF>;
+  constexpr int SD = FMT == kMixM ? kStageDw<QMV_Q6K> : kStageDw<FMT>;
+  static_assert(kStageDw<QMV_Q4K> <= kStageDw<QMV_Q6K>, "mixed staging size");
+  __shared__ uint32_t stage_lds[MW * SD];
+  __shared__ f32x4 red_raw[2][MW][32];  // [buffer][wave][lane pair] -> 2 x float2
+  float* red = reinterpret_cast<float*>(red_raw);
+  int si = 0;  // this workgroup's segment (workgroup-uniform scan)
+  for (int i = 1; i < tb.count; ++i) si = (int(blockIdx.x) >= tb.s[i].b0) ? i : si;
+  const MSeg& sg = tb.s[si];
+  if constexpr (FMT == kMixM) {
+    if (sg.fmt == QMV_Q6K) mfma_segment<QMV_Q6K, false, KF, SD>(tb, sg, stage_lds, red);
+    else mfma_segment<QMV_Q4K, false, KF, SD>(tb, sg, stage_lds, red);
+  } else {
+    mfma_segment<FMT, XF16, KF, SD>(tb, sg, stage_lds, red);
+  }
+}
+
 int blocks_override() {
   static const int v = [] {
     const char* e = getenv("QMV_MFMA_BLOCKS");  // A/B tuning only: workgroups per launch
@@ -515,6 +535,7 @@ bool launch_table(int fmt, MTable& t, int x_dtype, hipStream_t s, hipError_t* er
       return f16 ? pick_kf<QMV_W4A16_G64, true>(t, s, err) : pick_kf<QMV_W4A16_G64, false>(t, s, err);
     case QMV_Q4K: return pick_kf<QMV_Q4K, false>(t, s, err);
     case QMV_Q6K: return pick_kf<QMV_Q6K, false>(t, s, err);
+    case kMixM: return pick_kf<kMixM, false>(t, s, err);
     default: return false;
   }
 }
@@ -536,35 +557,62 @@ bool launch_matvec_mfma(int fmt, int64_t N, int64_t K, int nv, const uint8_t* W,
   t.count = 1;
   t.K = int(K);
   t.nv = nv;
-  t.s[0] = MSeg{W, p.off[1], p.off[2], p.off[3], x, y, int(N), 0, 0};
+  t.s[0] = MSeg{W, p.off[1], p.off[2], p.off[3], x, y, int(N), 0, 0, fmt};
   return launch_table(fmt, t, x_dtype, s, err);
 }
 
-// Several matvecs of one format, K and batch (>= 2) on the matrix cores: per
-// chunk of up to 8 vectors, one launch per kMaxSeg items.  Returns false
-// (nothing launched) when some item is outside the kernel's range.
+// Several matvecs of one K and batch (>= 2) on the matrix cores: per chunk of
+// up to 8 vectors, one launch per kMaxSeg items of one format (items of
+// different formats run in separate launch series; Q4K with Q6K share the
+// mixed kernel).  An item's format is its own fmt field, or `fmt` where that
+// is 0.  Returns false (nothing launched) when some item is outside the
+// kernel's range.
 bool launch_matvec_grouped_mfma(int fmt, int64_t K, int64_t batch, int count, const qmv_matvec_item* items,
                                 int x_dtype, hipStream_t s, hipError_t* err) {
+  auto eff = [&](int i) { return items[i].fmt ? items[i].fmt : fmt; };
   for (int i = 0; i < count; ++i)
-    if (!fits(fmt, items[i].N, K)) return false;
+    if (!fits(eff(i), items[i].N, K)) return false;
   const int64_t xel = (x_dtype == QMV_F16) ? 2 : 4;
-  for (int64_t b0 = 0; b0 < batch; b0 += 8) {
-    const int nv = int(batch - b0 < 8 ? batch - b0 : 8);
-    for (int i0 = 0; i0 < count; i0 += kMaxSeg) {
-      MTable t{};
-      t.K = int(K);
-      t.nv = nv;
-      t.count = count - i0 < kMaxSeg ? count - i0 : kMaxSeg;
-      for (int i = 0; i < t.count; ++i) {
-        const qmv_matvec_item& it = items[i0 + i];
-        const Planes p = planes_of(fmt, it.N, K);
-        t.s[i] = MSeg{static_cast<const uint8_t*>(it.W), p.off[1], p.off[2], p.off[3],
-                      static_cast<const uint8_t*>(it.x) + b0 * K * xel, static_cast<float*>(it.y) + b0 * it.N,
-                      int(it.N), 0, 0};
+  auto run = [&](int tfmt, const int* idx, int n) {
+    for (int64_t b0 = 0; b0 < batch; b0 += 8) {
+      const int nv = int(batch - b0 < 8 ? batch - b0 : 8);
+      for (int i0 = 0; i0 < n; i0 += kMaxSeg) {
+        MTable t{};
+        t.K = int(K);
+        t.nv = nv;
+        t.count = n - i0 < kMaxSeg ? n - i0 : kMaxSeg;
+        for (int j = 0; j < t.count; ++j) {
+          const int i = idx[i0 + j];
+          const qmv_matvec_item& it = items[i];
+          const Planes p = planes_of(eff(i), it.N, K);
+          t.s[j] = MSeg{static_cast<const uint8_t*>(it.W), p.off[1], p.off[2], p.off[3],
+                        static_cast<const uint8_t*>(it.x) + b0 * K * xel, static_cast<float*>(it.y) + b0 * it.N,
+                        int(it.N), 0, 0, eff(i)};
+        }
+        if (!launch_table(tfmt, t, x_dtype, s, err)) return false;
+        if (*err != hipSuccess) return true;
       }
-      if (!launch_table(fmt, t, x_dtype, s, err)) return false;
-      if (*err != hipSuccess) return true;
     }
+    return true;
+  };
+  constexpr int kMaxItems = 4096;  // host-side index scratch (the API caps count below this)
+  int idx[kMaxItems];
+  bool same = true, kquant = true;
+  for (int i = 0; i < count; ++i) {
+    same = same && eff(i) == eff(0);
+    kquant = kquant && (eff(i) == QMV_Q4K || eff(i) == QMV_Q6K);
+  }
+  if (same || kquant) {
+    for (int i = 0; i < count; ++i) idx[i] = i;
+    return run(same ? eff(0) : kMixM, idx, count);
+  }
+  for (int f = 1; f <= 4; ++f) {
+    int n = 0;
+    for (int i = 0; i < count; ++i)
+      if (eff(i) == f) idx[n++] = i;
+    if (n == 0) continue;
+    if (!run(f, idx, n)) return false;
+    if (*err != hipSuccess) return true;
   }
   return true;
 }

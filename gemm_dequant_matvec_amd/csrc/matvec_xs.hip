@@ -281,9 +281,11 @@ struct Seg {
   const void* x;
   float* y;
   int N;
-  int b0;  // first block of this segment
-  int nb;  // blocks of this segment
+  int b0;   // first block of this segment
+  int nb;   // blocks of this segment
+  int fmt;  // format (read by the mixed Q4K / Q6K kernel only)
 };
+constexpr int kMix = 0;  // FMT of a table mixing Q4K and Q6K segments
 struct SegTable {
   Seg s[kMaxSeg];
   int count;
@@ -294,21 +296,15 @@ struct SegTable {
 // (covers K = 32 * LPR * UPL, ragged tail masked); R rows per lane group; ONE:
 // the table holds one segment (its fields then load at fixed offsets, with no
 // scan in front of them).
-template <int FMT, bool XF16, int LPR, int UPL, int R, bool ONE>
-__global__ __launch_bounds__(kThreads) void matvec_xs_kernel(const SegTable t) {
+// This block's share of one segment (the body of the kernels below).
+template <int FMT, bool XF16, int LPR, int UPL, int R>
+__device__ __forceinline__ void xs_segment(const Seg& sg, const int K) {
   constexpr bool H2 = (FMT == QMV_W4A16_G64 && XF16);
   constexpr int RPW = 64 / LPR;
   const int lane = threadIdx.x & 63;
   const int sub = lane / LPR;
   const int l = lane % LPR;
-  const int K = t.K;
   const int U = K >> 5;
-
-  // this block's segment (block-uniform scan of at most kMaxSeg entries)
-  int si = 0;
-  if constexpr (!ONE)
-    for (int i = 1; i < t.count; ++i) si = (int(blockIdx.x) >= t.s[i].b0) ? i : si;
-  const Seg& sg = t.s[si];
   const Geo g{sg.W, sg.off1, sg.off2, sg.off3, K};
   const int N = sg.N;
   float* __restrict__ y = sg.y;
@@ -374,6 +370,26 @@ __global__ __launch_bounds__(kThreads) void matvec_xs_kernel(const SegTable t) {
   }
 }
 
+template <int FMT, bool XF16, int LPR, int UPL, int R, bool ONE>
+__global__ __launch_bounds__(kThreads) void matvec_xs_kernel(const SegTable t) {
+  // this block's segment (block-uniform scan of at most kMaxSeg entries)
+  int si = 0;
+  if constexpr (!ONE)
+    for (int i = 1; i < t.count; ++i) si = (int(blockIdx.x) >= t.s[i].b0) ? i : si;
+  xs_segment<FMT, XF16, LPR, UPL, R>(t.s[si], t.K);
+}
+
+// Q4K and Q6K segments in one launch (the K-quant mix of one decoder layer's
+// q / k / v projections): each block takes its own segment's format path.
+template <int LPR, int UPL, int R>
+__global__ __launch_bounds__(kThreads) void matvec_xs_mix_kernel(const SegTable t) {
+  int si = 0;
+  for (int i = 1; i < t.count; ++i) si = (int(blockIdx.x) >= t.s[i].b0) ? i : si;
+  const Seg& sg = t.s[si];
+  if (sg.fmt == QMV_Q6K) xs_segment<QMV_Q6K, false, LPR, UPL, R>(sg, t.K);
+  else xs_segment<QMV_Q4K, false, LPR, UPL, R>(sg, t.K);
+}
+
 template <int FMT, bool XF16, int LPR, int UPL, int R>
 hipError_t go(SegTable& t, hipStream_t s) {
   constexpr int rows_per_group = R * (64 / LPR);
@@ -398,7 +414,9 @@ hipError_t go(SegTable& t, hipStream_t s) {
     t.s[i].nb = int(std::max<int64_t>(1, std::min(need, share)));
     b += t.s[i].nb;
   }
-  if (t.count == 1)
+  if constexpr (FMT == kMix)
+    hipLaunchKernelGGL((matvec_xs_mix_kernel<LPR, UPL, R>), dim3(b), dim3(kThreads), 0, s, t);
+  else if (t.count == 1)
     hipLaunchKernelGGL((matvec_xs_kernel<FMT, XF16, LPR, UPL, R, true>), dim3(b), dim3(kThreads), 0, s, t);
   else
     hipLaunchKernelGGL((matvec_xs_kernel<FMT, XF16, LPR, UPL, R, false>), dim3(b), dim3(kThreads), 0, s, t);
@@ -471,6 +489,7 @@ bool launch_table(int fmt, SegTable& t, int x_dtype, hipStream_t s, hipError_t* 
       return f16 ? dispatch<QMV_W4A16_G64, true>(t, rsel, s, err) : dispatch<QMV_W4A16_G64, false>(t, rsel, s, err);
     case QMV_Q4K: return dispatch<QMV_Q4K, false>(t, rsel, s, err);
     case QMV_Q6K: return dispatch<QMV_Q6K, false>(t, rsel, s, err);
+    case kMix: return dispatch<kMix, false>(t, rsel, s, err);
     default: return false;
   }
 }
@@ -486,35 +505,62 @@ bool launch_matvec_b1(int fmt, int64_t N, int64_t K, const uint8_t* W, const voi
   SegTable t{};
   t.count = 1;
   t.K = int(K);
-  t.s[0] = Seg{W, p.off[1], p.off[2], p.off[3], x, y, int(N), 0, 0};
+  t.s[0] = Seg{W, p.off[1], p.off[2], p.off[3], x, y, int(N), 0, 0, fmt};
   return launch_table(fmt, t, x_dtype, s, err);
 }
 
-// Several single-vector matvecs of one format and one K in one launch per
-// kMaxSeg items.  Returns false (nothing launched) when the shape does not fit
-// the activation-stationary kernels.
+// Several single-vector matvecs of one K in one launch per kMaxSeg items.
+// Items of one format share a launch; items that are exactly Q4K and Q6K share
+// the mixed kernel; any other mix runs one launch series per format.  An item's
+// format is its own fmt field, or `fmt` where that is 0.  Returns false
+// (nothing launched) when the shape does not fit the activation-stationary
+// kernels.
 bool launch_matvec_grouped_b1(int fmt, int64_t K, int count, const qmv_matvec_item* items, int x_dtype,
                               hipStream_t s, hipError_t* err) {
   const int U = int(K) / 32;
   const int lpr = U >= 64 ? 64 : (U > 16 ? 32 : 16);
   const int upl = (U + lpr - 1) / lpr;
-  if (upl > ((fmt == QMV_W4A16_G64 && x_dtype == QMV_F16) ? 4 : 3)) return false;
-  // a launch takes up to kMaxSeg items and up to 2^30 rows
-  const int64_t max_rows = int64_t(1) << 30;
-  for (int i0 = 0; i0 < count;) {
-    SegTable t{};
-    t.K = int(K);
-    int64_t rows = 0;
-    while (t.count < kMaxSeg && i0 + t.count < count && (t.count == 0 || rows + items[i0 + t.count].N <= max_rows)) {
-      const qmv_matvec_item& it = items[i0 + t.count];
-      const Planes p = planes_of(fmt, it.N, K);
-      t.s[t.count++] = Seg{static_cast<const uint8_t*>(it.W), p.off[1], p.off[2], p.off[3], it.x,
-                           static_cast<float*>(it.y), int(it.N), 0, 0};
-      rows += it.N;
+  if (upl > (x_dtype == QMV_F16 ? 4 : 3)) return false;
+  auto eff = [&](int i) { return items[i].fmt ? items[i].fmt : fmt; };
+  // launches over the items with indices idx[0..n), as tables of format tfmt
+  auto run = [&](int tfmt, const int* idx, int n) {
+    const int64_t max_rows = int64_t(1) << 30;  // a launch takes up to kMaxSeg items and 2^30 rows
+    for (int i0 = 0; i0 < n;) {
+      SegTable t{};
+      t.K = int(K);
+      int64_t rows = 0;
+      while (t.count < kMaxSeg && i0 + t.count < n && (t.count == 0 || rows + items[idx[i0 + t.count]].N <= max_rows)) {
+        const int i = idx[i0 + t.count];
+        const qmv_matvec_item& it = items[i];
+        const Planes p = planes_of(eff(i), it.N, K);
+        t.s[t.count++] = Seg{static_cast<const uint8_t*>(it.W), p.off[1], p.off[2], p.off[3], it.x,
+                             static_cast<float*>(it.y), int(it.N), 0, 0, eff(i)};
+        rows += it.N;
+      }
+      if (!launch_table(tfmt, t, x_dtype, s, err)) return false;
+      if (*err != hipSuccess) return true;
+      i0 += t.count;
     }
-    if (!launch_table(fmt, t, x_dtype, s, err)) return false;
+    return true;
+  };
+  constexpr int kMaxItems = 4096;  // host-side index scratch (the API caps count below this)
+  int idx[kMaxItems];
+  bool same = true, kquant = true;
+  for (int i = 0; i < count; ++i) {
+    same = same && eff(i) == eff(0);
+    kquant = kquant && (eff(i) == QMV_Q4K || eff(i) == QMV_Q6K);
+  }
+  if (same || kquant) {
+    for (int i = 0; i < count; ++i) idx[i] = i;
+    return run(same ? eff(0) : kMix, idx, count);
+  }
+  for (int f = 1; f <= 4; ++f) {  // one launch series per format present
+    int n = 0;
+    for (int i = 0; i < count; ++i)
+      if (eff(i) == f) idx[n++] = i;
+    if (n == 0) continue;
+    if (!run(f, idx, n)) return false;
     if (*err != hipSuccess) return true;
-    i0 += t.count;
   }
   return true;
 }

@@ -85,7 +85,7 @@
 extern "C" {
 #endif
 
-#define QMV_ABI_VERSION 1
+#define QMV_ABI_VERSION 2
 #define QMV_LAYOUT_VERSION 1
 
 enum qmv_format {
@@ -126,6 +126,7 @@ typedef struct qmv_matvec_item {
   const void* W; /* packed matrix, layout above, 16-byte aligned */
   const void* x; /* [batch][K] activations; items may share one x */
   void* y;       /* [batch][N] output; must not overlap another item's y */
+  int32_t fmt;   /* this matrix's qmv_format, or 0 for the call's fmt */
 } qmv_matvec_item;
 
 /* ABI version (QMV_ABI_VERSION); *layout_version receives QMV_LAYOUT_VERSION if non-NULL. */
@@ -169,17 +170,21 @@ int qmv_matvec(int fmt, int64_t N, int64_t K, int64_t batch, const void* W,
                const void* x, int x_dtype, void* y, int y_dtype, void* stream);
 
 /*
- * Several matvecs of one format, one K and one batch in as few launches as
- * possible: for every item i, y_i[b][n] = sum_k W_i[n][k] * x_i[b][k].
+ * Several matvecs of one K and one batch in as few launches as possible: for
+ * every item i, y_i[b][n] = sum_k W_i[n][k] * x_i[b][k].
  * The grouped dispatch of the pages' decoders: the q / k / v projections in
  * one dispatch with the simdgroups spread over the three matrices, gate / up
- * in another (aot-llm README, Metal backend notes).  Up to 16 items share
- * one launch (per chunk of 8 vectors at batch >= 2); the launch's workgroups
- * are split over the items in proportion to their rows.  Items outside the
- * grouped kernels' range (K above 6144 at batch >= 2, or an activation slice
- * too wide for registers at batch 1) run one qmv_matvec launch each.  Each
- * item's result equals its qmv_matvec result bit for bit.  Dtypes and
- * alignment as qmv_matvec; count >= 1.
+ * in another (aot-llm README, Metal backend notes).  An item's format is its
+ * own fmt field, or the call's `fmt` where that field is 0 (`fmt` may be 0
+ * only if every item names its own).  Up to 16 items share one launch (per
+ * chunk of 8 vectors at batch >= 2); the launch's workgroups are split over
+ * the items in proportion to their rows.  Q4K and Q6K items may share a
+ * launch (a layer whose v projection is Q6K next to Q4K q and k); other mixes
+ * run one launch series per format.  Items outside the grouped kernels' range
+ * (K above 6144 at batch >= 2, or an activation slice too wide for registers
+ * at batch 1) run one qmv_matvec launch each.  Each item's result equals its
+ * qmv_matvec result bit for bit.  Dtypes and alignment as qmv_matvec (x_dtype
+ * must suit every item's format); 1 <= count <= 4096.
  * Errors: FORMAT, SHAPE, NULL, ALIGN, DTYPE, UNSUPPORTED, OVERFLOW, DEVICE, LAUNCH
  * (the message names the offending item).
  */
@@ -188,9 +193,10 @@ int qmv_matvec_grouped(int fmt, int64_t K, int64_t batch, int count, const qmv_m
 
 /*
  * Y[m][n] = sum_k X[m][k] * W[n][k] for m < M, on bf16 matrix cores with f32
- * accumulation; weight tiles are dequantized once per tile into LDS (aot-llm
- * README, Metal backend notes: prompt batches use a tiled GEMM on the matrix
- * units with the weights dequantized once per tile).
+ * accumulation; each weight is dequantized once per token tile, in registers,
+ * straight into the matrix-core operand (aot-llm README, Metal backend notes:
+ * prompt batches use a tiled GEMM on the matrix units with the weights
+ * dequantized once per tile).
  *   fmt   QMV_W4A16_G64 (others -> UNSUPPORTED)
  *   X     [M][K] of x_dtype QMV_BF16, device, 16-byte aligned
  *   Y     [M][N] of y_dtype QMV_BF16, device, 4-byte aligned

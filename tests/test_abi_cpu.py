@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(q):
 
 
 def test_abi_and_status_strings(q):
-    assert q.abi_version() == (1, 1)
+    assert q.abi_version() == (2, 1)
     for st in range(0, -10, -1):
         assert q._lib.qmv_status_string(st).decode() not in ("", "unknown status")
     assert q._lib.qmv_status_string(-99).decode() == "unknown status"
@@ -123,3 +123,26 @@ def test_grouped_argument_errors(q):
     items[1].N = 64
     assert call(3, 200, 1, 2, items, 1, 1, None) == -4
     assert call(3, 256, 1, 2, items, 2, 1, None) == -3
+    assert call(3, 256, 1, 4097, items, 1, 1, None) == -4
+
+
+def test_grouped_item_format_errors(q):
+    # each item's format is its own fmt field, or the call's where that is 0
+    assert ctypes.sizeof(q.QmvMatvecItem) == 40
+    P = 1 << 20
+    items = (q.QmvMatvecItem * 3)()
+    for it in items:
+        it.N, it.W, it.x, it.y, it.fmt = 64, P, P, P, 0
+    call = lambda *a: q.raw_call("qmv_matvec_grouped", *a)  # noqa: E731
+    assert call(0, 256, 1, 3, items, 1, 1, None) == -2  # no format anywhere
+    assert "items[0].fmt" in q.last_error()
+    items[0].fmt = items[1].fmt = 3
+    assert call(0, 256, 1, 3, items, 1, 1, None) == -2
+    assert "items[2]" in q.last_error()
+    items[2].fmt = 9
+    assert call(4, 256, 1, 3, items, 1, 1, None) == -2
+    items[2].fmt = 2  # W4A16 beside Q4K: f16 activations suit only the W4A16 item
+    assert call(0, 256, 1, 3, items, 2, 1, None) == -3
+    assert "items[0]" in q.last_error()
+    assert call(0, 64, 1, 3, items, 1, 1, None) == -4  # K = 64 is no Q4K block multiple
+    assert "Q4K" in q.last_error() or "q4k" in q.last_error().lower()

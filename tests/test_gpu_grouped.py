@@ -1,5 +1,6 @@
-"""GPU parity of the grouped matvec (several matrices of one format and K per
-call) against the CPU oracle, and against one qmv_matvec call per matrix.
+"""GPU parity of the grouped matvec (several matrices of one K per call, one
+format or several) against the CPU oracle, and against one qmv_matvec call
+per matrix.
 
 Bar: every output within 1e-3 * ||W_row|| * ||x|| of the f64 oracle; with
 the same inputs the grouped call returns exactly what the single calls
@@ -176,25 +177,77 @@ def test_config_w4a16_gate_up_grouped(qmv):
         assert r["ok"], r
 
 
-def test_config_decode_layer_qkv_grouped(qmv):
-    # q and k (Q4K) of one 1.1B decoder layer in one call, v (Q6K) in another
+@pytest.mark.parametrize("batch", [1, 8])
+def test_config_decode_layer_qkv_grouped(qmv, batch):
+    # q and k (Q4K) and v (Q6K) of one 1.1B decoder layer in one mixed call;
+    # each output equals its own single call bit for bit
     layer = [m for m in wl.c5_sweep(1, layers=1)["mats"] if m[0] in ("l0.q", "l0.k", "l0.v")]
-    x = wl.gen_x(2048, 1, "f32", (31, 0, 0))
+    x = wl.gen_x(2048, batch, "f32", (31, 0, 0))
     xt = dev_x(x, "f32")
     xv = x_values(x, "f32")
     ws = {nm: wl.gen_weights(fmt, N, K, key) for nm, fmt, N, K, key in layer}
-    fmts = {nm: (fmt, N) for nm, fmt, N, K, key in layer}
-    yq, yk = qmv.matvec_grouped("q4k", [(pack_dev(qmv, "q4k", ws[n]), xt, fmts[n][1]) for n in ("l0.q", "l0.k")],
-                                2048)
-    (yv,) = qmv.matvec_grouped("q6k", [(pack_dev(qmv, "q6k", ws["l0.v"]), xt, 256)], 2048)
+    Wp = {nm: pack_dev(qmv, fmt, ws[nm]) for nm, fmt, N, K, key in layer}
+    ys = qmv.matvec_grouped(None, [(Wp[nm], xt, N, None, fmt) for nm, fmt, N, K, key in layer], 2048)
     torch.cuda.synchronize()
-    for nm, y in (("l0.q", yq), ("l0.k", yk), ("l0.v", yv)):
-        fmt, N = fmts[nm]
+    for (nm, fmt, N, K, key), y in zip(layer, ys):
         W32 = oracle.dequant_rows(fmt, ws[nm], np.arange(N))
         r = oracle.check_within(y.cpu().numpy(), oracle.matvec_ref(W32, xv),
                                 oracle.tolerance_bound(W32, xv, TAU["matvec"]))
-        _say(nm, r)
+        _say(nm, batch, r)
         assert r["ok"], (nm, r)
+        single = qmv.matvec(fmt, Wp[nm], xt, N, K)
+        torch.cuda.synchronize()
+        assert torch.equal(single.view(torch.int32), y.view(torch.int32)), nm
+
+
+@pytest.mark.parametrize("batch", [1, 3, 8, 11])
+def test_grouped_mixed_kquant_ragged(qmv, batch):
+    # Q4K and Q6K items interleaved in one call (one launch per 16 items and
+    # chunk of 8 vectors), ragged rows, K over several super-blocks
+    K = 256 * 6
+    fmts = ["q4k", "q6k", "q6k", "q4k", "q6k"] * 4  # 20 items: two launches at batch 1
+    shapes = [int(n) for n in np.random.default_rng(12).integers(1, 180, len(fmts))]
+    x = wl.gen_x(K, batch, "f32", (32, batch, 0))
+    xt = dev_x(x, "f32")
+    xv = x_values(x, "f32")
+    ws = [wl.gen_weights(f, n, K, (32, batch, i + 1)) for i, (f, n) in enumerate(zip(fmts, shapes))]
+    Wp = [pack_dev(qmv, f, w) for f, w in zip(fmts, ws)]
+    ys = qmv.matvec_grouped("q4k", [(Wp[i], xt, shapes[i], None, None if fmts[i] == "q4k" else "q6k")
+                                    for i in range(len(fmts))], K)
+    torch.cuda.synchronize()
+    _say(batch, shapes)
+    for i, (f, n, w, y) in enumerate(zip(fmts, shapes, ws, ys)):
+        W32 = oracle.dequant_rows(f, w, np.arange(n))
+        r = oracle.check_within(y.cpu().numpy(), oracle.matvec_ref(W32, xv),
+                                oracle.tolerance_bound(W32, xv, TAU["matvec"]))
+        assert r["ok"], (i, f, n, r)
+        single = qmv.matvec(f, Wp[i], xt, n, K)
+        torch.cuda.synchronize()
+        assert torch.equal(single.view(torch.int32), y.view(torch.int32)), (i, f, n)
+
+
+@pytest.mark.parametrize("batch", [1, 8])
+def test_grouped_mixed_other_formats_split(qmv, batch):
+    # Q8_0, W4A16 (f32 activations) and Q4K in one call: one launch series per
+    # format, results as their single calls
+    K = 2048
+    fmts = ["q8_0", "w4a16_g64", "q4k", "q8_0", "w4a16_g64"]
+    shapes = [100, 257, 64, 3, 1000]
+    x = wl.gen_x(K, batch, "f32", (33, batch, 0))
+    xt = dev_x(x, "f32")
+    xv = x_values(x, "f32")
+    ws = [wl.gen_weights(f, n, K, (33, batch, i + 1)) for i, (f, n) in enumerate(zip(fmts, shapes))]
+    Wp = [pack_dev(qmv, f, w) for f, w in zip(fmts, ws)]
+    ys = qmv.matvec_grouped(None, [(Wp[i], xt, shapes[i], None, fmts[i]) for i in range(len(fmts))], K)
+    torch.cuda.synchronize()
+    for i, (f, n, w, y) in enumerate(zip(fmts, shapes, ws, ys)):
+        W32 = oracle.dequant_rows(f, w, np.arange(n))
+        r = oracle.check_within(y.cpu().numpy(), oracle.matvec_ref(W32, xv),
+                                oracle.tolerance_bound(W32, xv, TAU["matvec"]))
+        assert r["ok"], (i, f, n, r)
+        single = qmv.matvec(f, Wp[i], xt, n, K)
+        torch.cuda.synchronize()
+        assert torch.equal(single.view(torch.int32), y.view(torch.int32)), (i, f, n)
 
 
 @pytest.mark.parametrize("batch", [1, 8])
