@@ -293,12 +293,16 @@ struct SegTable {
 };
 
 // FMT / XF16: format and activation type; LPR lanes per row; UPL units per lane
-// (covers K = 32 * LPR * UPL, ragged tail masked); R rows per lane group; ONE:
-// the table holds one segment (its fields then load at fixed offsets, with no
-// scan in front of them).
+// (covers K = 32 * LPR * UPL * KS, ragged tail masked); R rows per lane group;
+// KS: waves that split K between them (1: every wave walks its own row groups
+// over the whole of K; KS > 1: the KS waves of a block each take one slice
+// of K for the same row groups and their partial sums meet in LDS, added in
+// slice order); ONE: the table holds one segment (its fields then load at
+// fixed offsets, with no scan in front of them).
 // This block's share of one segment (the body of the kernels below).
-template <int FMT, bool XF16, int LPR, int UPL, int R>
+template <int FMT, bool XF16, int LPR, int UPL, int R, int KS>
 __device__ __forceinline__ void xs_segment(const Seg& sg, const int K) {
+  constexpr int TPB = KS == 1 ? kWaves : 1;  // independent lane-group teams per block
   constexpr bool H2 = (FMT == QMV_W4A16_G64 && XF16);
   constexpr int RPW = 64 / LPR;
   const int lane = threadIdx.x & 63;
@@ -310,14 +314,18 @@ __device__ __forceinline__ void xs_segment(const Seg& sg, const int K) {
   float* __restrict__ y = sg.y;
   const int ngroups = (N + R * RPW - 1) / (R * RPW);
   // wave-uniform (readfirstlane): the loop's branches and loads stay scalar-controlled
-  const int gw = (int(blockIdx.x) - sg.b0) * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int TW = sg.nb * kWaves;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gw = (int(blockIdx.x) - sg.b0) * TPB + (KS == 1 ? wv : 0);
+  const int TW = sg.nb * TPB;
+  const int ks = KS == 1 ? 0 : wv;  // K slice of this wave
+  __shared__ float red[2][KS][RPW * R];
+  int par = 0;
 
   int uu[UPL], sh[UPL];
   bool uv[UPL];
 #pragma unroll
   for (int j = 0; j < UPL; ++j) {
-    const int u = l + j * LPR;
+    const int u = (ks * UPL + j) * LPR + l;
     uv[j] = u < U;
     uu[j] = uv[j] ? u : U - 1;
     sh[j] = 6 * (uu[j] & 7);
@@ -354,7 +362,25 @@ __device__ __forceinline__ void xs_segment(const Seg& sg, const int K) {
     for (int r = 0; r < R; ++r) {
       const float tot = group_sum<LPR>(acc[r], sub);
       const int row = gi * (R * RPW) + r * RPW + sub;
-      if (l == 0 && row < N) y[row] = tot;
+      if constexpr (KS == 1) {
+        if (l == 0 && row < N) y[row] = tot;
+      } else {
+        if (l == 0) red[par][ks][r * RPW + sub] = tot;
+      }
+    }
+    if constexpr (KS > 1) {  // every wave of the block runs the same groups: uniform barrier
+      __syncthreads();
+      if (ks == 0 && l == 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int row = gi * (R * RPW) + r * RPW + sub;
+          float t = 0.0f;
+#pragma unroll
+          for (int w = 0; w < KS; ++w) t += red[par][w][r * RPW + sub];
+          if (row < N) y[row] = t;
+        }
+      }
+      par ^= 1;  // the next group writes the other buffer while this one is read
     }
   };
   // the next group's loads are in flight while the current one is reduced
@@ -370,28 +396,30 @@ __device__ __forceinline__ void xs_segment(const Seg& sg, const int K) {
   }
 }
 
-template <int FMT, bool XF16, int LPR, int UPL, int R, bool ONE>
-__global__ __launch_bounds__(kThreads) void matvec_xs_kernel(const SegTable t) {
+template <int FMT, bool XF16, int LPR, int UPL, int R, bool ONE, int KS>
+__global__ __launch_bounds__(KS == 1 ? kThreads : 64 * KS) void matvec_xs_kernel(const SegTable t) {
   // this block's segment (block-uniform scan of at most kMaxSeg entries)
   int si = 0;
   if constexpr (!ONE)
     for (int i = 1; i < t.count; ++i) si = (int(blockIdx.x) >= t.s[i].b0) ? i : si;
-  xs_segment<FMT, XF16, LPR, UPL, R>(t.s[si], t.K);
+  xs_segment<FMT, XF16, LPR, UPL, R, KS>(t.s[si], t.K);
 }
 
 // Q4K and Q6K segments in one launch (the K-quant mix of one decoder layer's
 // q / k / v projections): each block takes its own segment's format path.
-template <int LPR, int UPL, int R>
-__global__ __launch_bounds__(kThreads) void matvec_xs_mix_kernel(const SegTable t) {
+template <int LPR, int UPL, int R, int KS>
+__global__ __launch_bounds__(KS == 1 ? kThreads : 64 * KS) void matvec_xs_mix_kernel(const SegTable t) {
   int si = 0;
   for (int i = 1; i < t.count; ++i) si = (int(blockIdx.x) >= t.s[i].b0) ? i : si;
   const Seg& sg = t.s[si];
-  if (sg.fmt == QMV_Q6K) xs_segment<QMV_Q6K, false, LPR, UPL, R>(sg, t.K);
-  else xs_segment<QMV_Q4K, false, LPR, UPL, R>(sg, t.K);
+  if (sg.fmt == QMV_Q6K) xs_segment<QMV_Q6K, false, LPR, UPL, R, KS>(sg, t.K);
+  else xs_segment<QMV_Q4K, false, LPR, UPL, R, KS>(sg, t.K);
 }
 
-template <int FMT, bool XF16, int LPR, int UPL, int R>
+template <int FMT, bool XF16, int LPR, int UPL, int R, int KS>
 hipError_t go(SegTable& t, hipStream_t s) {
+  constexpr int BW = KS == 1 ? kWaves : KS;   // waves per block
+  constexpr int TPB = KS == 1 ? kWaves : 1;   // row-group teams per block
   constexpr int rows_per_group = R * (64 / LPR);
   int64_t groups[kMaxSeg], total = 0;
   for (int i = 0; i < t.count; ++i) {
@@ -404,22 +432,22 @@ hipError_t go(SegTable& t, hipStream_t s) {
   // take two groups; the f32-activation paths and the large heads ran slower
   // with more waves).
   constexpr bool H2 = (FMT == QMV_W4A16_G64 && XF16);
-  const int64_t max_blocks = 256 * ((H2 && total <= 256 * 24) ? 24 : 16) / kWaves;
-  const int64_t budget = std::min<int64_t>((total + kWaves - 1) / kWaves, max_blocks);
+  const int64_t max_blocks = 256 * ((H2 && total * KS <= 256 * 24) ? 24 : 16) / BW;
+  const int64_t budget = std::min<int64_t>((total + TPB - 1) / TPB, max_blocks);
   int b = 0;
   for (int i = 0; i < t.count; ++i) {
-    const int64_t need = (groups[i] + kWaves - 1) / kWaves;
+    const int64_t need = (groups[i] + TPB - 1) / TPB;
     const int64_t share = (budget * groups[i] + total - 1) / total;
     t.s[i].b0 = b;
     t.s[i].nb = int(std::max<int64_t>(1, std::min(need, share)));
     b += t.s[i].nb;
   }
   if constexpr (FMT == kMix)
-    hipLaunchKernelGGL((matvec_xs_mix_kernel<LPR, UPL, R>), dim3(b), dim3(kThreads), 0, s, t);
+    hipLaunchKernelGGL((matvec_xs_mix_kernel<LPR, UPL, R, KS>), dim3(b), dim3(64 * BW), 0, s, t);
   else if (t.count == 1)
-    hipLaunchKernelGGL((matvec_xs_kernel<FMT, XF16, LPR, UPL, R, true>), dim3(b), dim3(kThreads), 0, s, t);
+    hipLaunchKernelGGL((matvec_xs_kernel<FMT, XF16, LPR, UPL, R, true, KS>), dim3(b), dim3(64 * BW), 0, s, t);
   else
-    hipLaunchKernelGGL((matvec_xs_kernel<FMT, XF16, LPR, UPL, R, false>), dim3(b), dim3(kThreads), 0, s, t);
+    hipLaunchKernelGGL((matvec_xs_kernel<FMT, XF16, LPR, UPL, R, false, KS>), dim3(b), dim3(64 * BW), 0, s, t);
   return hipGetLastError();
 }
 
@@ -429,14 +457,22 @@ hipError_t go(SegTable& t, hipStream_t s) {
 // the launch is latency-bound and waves count), else two (twice the loads in
 // flight per wave, half the activation reloads), four for Q6K from 16384 slots
 // (the 32000 x 2048 head: 5 % faster than two).
-template <int FMT, bool XF16, int LPR, int UPL>
+template <int FMT, bool XF16, int LPR, int UPL, int KS = 1>
 hipError_t pick_r(SegTable& t, int rsel, hipStream_t s) {
   int64_t rows = 0;
   for (int i = 0; i < t.count; ++i) rows += t.s[i].N;
   const int64_t slots = rows / (64 / LPR);
   const int r = rsel ? rsel : slots <= 1024 ? 1 : (FMT == QMV_Q6K && slots >= 16384) ? 4 : 2;
-  if (r == 4) return go<FMT, XF16, LPR, UPL, 4>(t, s);
-  return r == 2 ? go<FMT, XF16, LPR, UPL, 2>(t, s) : go<FMT, XF16, LPR, UPL, 1>(t, s);
+  if (r == 4) return go<FMT, XF16, LPR, UPL, 4, KS>(t, s);
+  return r == 2 ? go<FMT, XF16, LPR, UPL, 2, KS>(t, s) : go<FMT, XF16, LPR, UPL, 1, KS>(t, s);
+}
+
+bool ksplit_off() {
+  static const bool v = [] {
+    const char* e = getenv("QMV_MATVEC_KSPLIT");  // A/B tuning only: 0 keeps K in one wave
+    return e && atoi(e) == 0;
+  }();
+  return v;
 }
 
 template <int FMT, bool XF16>
@@ -453,6 +489,17 @@ bool dispatch(SegTable& t, int rsel, hipStream_t s, hipError_t* e) {
   const int upl = (U + lpr - 1) / lpr;
   // activation registers per unit: 17 (fp16 pairs) or 34 (f32)
   if (upl > (H2 ? 4 : 3)) return false;
+  // Wide K (more than one unit per lane): split K over upl waves of one unit
+  // each instead (measured on MI355X, 2048 x 5632 down projections: W4A16
+  // 4.64 -> 4.24 us, Q6K 7.46 -> 7.15 us): less work and fewer activation
+  // registers per wave, and a wave's partial sum is ready sooner.
+  if (lpr == 64 && upl >= 2 && !ksplit_off()) {
+    switch (upl) {
+      case 2: *e = pick_r<FMT, XF16, 64, 1, 2>(t, rsel, s); return true;
+      case 3: *e = pick_r<FMT, XF16, 64, 1, 3>(t, rsel, s); return true;
+      default: *e = pick_r<FMT, XF16, 64, 1, 4>(t, rsel, s); return true;
+    }
+  }
   if (lpr == 64) {
     switch (upl) {
       case 1: *e = pick_r<FMT, XF16, 64, 1>(t, rsel, s); return true;
