@@ -140,6 +140,50 @@ def test_batched_matvec_k_ranges(qmv, fmt, kcase, batch):
         assert r["ok"], (fmt, K, batch, xd, r)
 
 
+# K cases of the single-vector kernel: one 32-weight unit per lane, K split
+# over 2 waves with a ragged second slice, over 2 and 3 waves in full, the
+# largest K with activations held in registers (4 waves for fp16 W4A16), and a
+# K past it (another kernel)
+B1_K = {
+    "q8_0": [2048, 2080, 4096, 6144, 6176],
+    "w4a16_g64": [2048, 2112, 4096, 5632, 8192, 8256],
+    "q4k": [2048, 2304, 4096, 5632, 6144, 6400],
+    "q6k": [2048, 2304, 4096, 5632, 6144, 6400],
+}
+
+
+@pytest.mark.parametrize("fmt", wl.FORMATS)
+@pytest.mark.parametrize("kcase", range(6))
+def test_single_vector_k_ranges(qmv, fmt, kcase):
+    if kcase >= len(B1_K[fmt]):
+        pytest.skip("no such case for this format")
+    K = B1_K[fmt][kcase]
+    for N in (1, 133):
+        w = wl.gen_weights(fmt, N, K, (23, kcase, N))
+        for xd in XDT[fmt]:
+            x = wl.gen_x(K, 1, xd, (23, kcase, N))
+            _say("b1", fmt, N, K, xd)
+            r, _, _ = check_matvec(qmv, fmt, w, x, xd)
+            assert r["ok"], (fmt, N, K, xd, r)
+
+
+@pytest.mark.parametrize("fmt", ["w4a16_g64", "q6k"])
+def test_one_hot_through_k_split_bit_exact(qmv, fmt):
+    # K = 5632 runs split over three waves: every column still comes back
+    # exactly as the dequantized weight
+    N, K = 40, 5632
+    w = wl.gen_weights(fmt, N, K, (24, 0, 0))
+    Wp = pack_dev(qmv, fmt, w)
+    W32 = oracle.dequant(fmt, w)
+    xd = XDT[fmt][0]
+    for k in (0, 2047, 2048, 4095, 4096, K - 1):
+        x = np.zeros((1, K), np.float64)
+        x[0, k] = 1.0
+        xb = x.astype(np.float32) if xd == "f32" else wl.to_f16_bits(x)
+        y = qmv.matvec(fmt, Wp, dev_x(xb, xd), N, K).cpu().numpy()
+        assert np.array_equal(y[0], W32[:, k]), (fmt, k)
+
+
 @pytest.mark.parametrize("fmt", wl.FORMATS)
 def test_one_hot_returns_dequantized_column_bit_exact(qmv, fmt):
     N, K = 70, wl.BLOCK[fmt] * 8 if fmt != "w4a16_g64" else 2048
