@@ -227,6 +227,26 @@ def test_grouped_mixed_kquant_ragged(qmv, batch):
 
 
 @pytest.mark.parametrize("batch", [1, 8])
+def test_grouped_mixed_outside_kernel_range_falls_back(qmv, batch):
+    # Q4K / Q6K mix at K = 6400: past the batched kernel's K and the single-vector
+    # kernel's register budget for f32 activations, so one launch per item
+    K = 6400
+    fmts, shapes = ["q4k", "q6k", "q4k"], [40, 9, 130]
+    x = wl.gen_x(K, batch, "f32", (34, batch, 0))
+    xt = dev_x(x, "f32")
+    xv = x_values(x, "f32")
+    ws = [wl.gen_weights(f, n, K, (34, batch, i + 1)) for i, (f, n) in enumerate(zip(fmts, shapes))]
+    Wp = [pack_dev(qmv, f, w) for f, w in zip(fmts, ws)]
+    ys = qmv.matvec_grouped(None, [(Wp[i], xt, shapes[i], None, fmts[i]) for i in range(3)], K)
+    torch.cuda.synchronize()
+    for i, (f, n, w, y) in enumerate(zip(fmts, shapes, ws, ys)):
+        W32 = oracle.dequant_rows(f, w, np.arange(n))
+        r = oracle.check_within(y.cpu().numpy(), oracle.matvec_ref(W32, xv),
+                                oracle.tolerance_bound(W32, xv, TAU["matvec"]))
+        assert r["ok"], (i, f, n, r)
+
+
+@pytest.mark.parametrize("batch", [1, 8])
 def test_grouped_mixed_other_formats_split(qmv, batch):
     # Q8_0, W4A16 (f32 activations) and Q4K in one call: one launch series per
     # format, results as their single calls
