@@ -416,6 +416,20 @@ __device__ __forceinline__ void mfma_segment(const MTable& tb, const MSeg& sg, u
           v[4 * s + e] = __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, t[2 * e + 1]) & odd) |
                                                        (__builtin_bit_cast(uint32_t, t[2 * e]) & ~odd));
       }
+    } else if constexpr (!XF16) {
+      // f32 x: the two lanes of a high / low pair need the same 8 values; each
+      // loads one half and takes the other from its partner (DPP swap of
+      // adjacent lanes), halving the activation traffic
+      const int k0 = (FMT == QMV_W4A16_G64) ? 64 * (uc >> 1) + 16 * G + 8 * (uc & 1) : 32 * uc + 8 * G;
+      const f32x4 mine = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.x) + xrow + k0 + 4 * low);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float m = ok ? mine[i] : 0.0f;
+        const float o = __builtin_bit_cast(
+            float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, m), 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+        v[i] = low ? o : m;
+        v[4 + i] = low ? m : o;
+      }
     } else {
       const int k0 = (FMT == QMV_W4A16_G64) ? 64 * (uc >> 1) + 16 * G + 8 * (uc & 1) : 32 * uc + 8 * G;
       load_x8<XF16>(a.x, xrow + k0, ok, v);
