@@ -40,6 +40,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -82,6 +83,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 
 // High or low bf16 part of two activations, packed.
+// The value of lane l ^ 16 (ds_swizzle, bit-mask mode: and 0x1F, xor 0x10).
+__device__ __forceinline__ float swap_rows(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+}
+
+// The value of the adjacent lane (0 <-> 1, 2 <-> 3, ...): DPP quad_perm [1,0,3,2].
+__device__ __forceinline__ float swap_pair(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ uint32_t part_pair(float a, float b, bool low) {
   const float ha = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, a) & 0xFFFF0000u);
   const float hb = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, b) & 0xFFFF0000u);
@@ -407,26 +418,40 @@ __device__ __forceinline__ void mfma_segment(const MTable& tb, const MSeg& sg, u
     float v[8];
     if constexpr (FMT == QMV_Q6K) {  // f32 x: k = 32u + 16s + 8(G/2) + (G%2) + 2e
       const uint32_t odd = 0u - static_cast<uint32_t>(G & 1);
+      // the 8 consecutive values of a sub-block are needed by four lanes: the
+      // high / low pair (adjacent lanes) of both lane groups G and G ^ 1 (16
+      // lanes apart); each loads two and the rest arrive by a DPP pair swap and
+      // a ds_swizzle across the 16-lane rows
+      const int par = G & 1;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         float t[8];
-        load_x8<false>(a.x, xrow + 32 * uc + 16 * s + 8 * (G >> 1), ok, t);
+        const f32x2 mine = *reinterpret_cast<const f32x2*>(static_cast<const float*>(a.x) + xrow + 32 * uc + 16 * s +
+                                                           8 * (G >> 1) + 4 * par + 2 * low);
+        const float m0 = ok ? mine[0] : 0.0f, m1 = ok ? mine[1] : 0.0f;
+        const float o0 = swap_pair(m0), o1 = swap_pair(m1);
+        const float h[4] = {low ? o0 : m0, low ? o1 : m1, low ? m0 : o0, low ? m1 : o1};  // values 4 par ..
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float g = swap_rows(h[i]);  // values 4 (par ^ 1) + i
+          t[i] = par ? g : h[i];
+          t[4 + i] = par ? h[i] : g;
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e)  // odd or even element by mask (a select would become a lane-varying index)
           v[4 * s + e] = __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, t[2 * e + 1]) & odd) |
                                                        (__builtin_bit_cast(uint32_t, t[2 * e]) & ~odd));
       }
     } else if constexpr (!XF16) {
-      // f32 x: the two lanes of a high / low pair need the same 8 values; each
-      // loads one half and takes the other from its partner (DPP swap of
-      // adjacent lanes), halving the activation traffic
+      // f32 x: the two lanes of a high / low pair (adjacent lanes) need the same
+      // 8 values; each loads one half and takes the other from its partner,
+      // halving the activation traffic
       const int k0 = (FMT == QMV_W4A16_G64) ? 64 * (uc >> 1) + 16 * G + 8 * (uc & 1) : 32 * uc + 8 * G;
       const f32x4 mine = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.x) + xrow + k0 + 4 * low);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float m = ok ? mine[i] : 0.0f;
-        const float o = __builtin_bit_cast(
-            float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, m), 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+        const float o = swap_pair(m);
         v[i] = low ? o : m;
         v[4 + i] = low ? m : o;
       }
