@@ -250,10 +250,14 @@ __device__ __forceinline__ float unit_dot(const Raw<FMT>& w, const XUnit<FMT == 
       const float s = f16_bits_to_f32(w.sz & 0xFFFFu), z = f16_bits_to_f32(w.sz >> 16);
       return fmaf(s, fmaf(-z, xu.s0, qa), acc);
     } else if constexpr (FMT == QMV_Q4K) {
-      const uint64_t lo = uint64_t(w.meta.y) | (uint64_t(w.meta.z) << 32);
-      const uint64_t hi = uint64_t(w.meta.z >> 16) | (uint64_t(w.meta.w) << 16);
-      const float sc = static_cast<float>(static_cast<uint32_t>(lo >> sh) & 63u);
-      const float m = static_cast<float>(static_cast<uint32_t>(hi >> sh) & 63u);
+      // sc_j sits at bit 6j and m_j at bit 48 + 6j of the 96-bit field {w, z, y};
+      // 32-bit funnel shifts read them from any word pair.  (A 64-bit shift
+      // wants an aligned register pair, so the compiler copied the loaded words
+      // and had to wait for the load right after issuing it.)
+      const uint32_t sa = sh < 32 ? w.meta.y : w.meta.z, sb = sh < 32 ? w.meta.z : w.meta.w;
+      const uint32_t ma = sh < 16 ? w.meta.z : w.meta.w;
+      const float sc = static_cast<float>(__builtin_amdgcn_alignbit(sb, sa, uint32_t(sh) & 31u) & 63u);
+      const float m = static_cast<float>(__builtin_amdgcn_alignbit(w.meta.w, ma, uint32_t(sh + 16) & 31u) & 63u);
       const float ds = f16_bits_to_f32(w.meta.x & 0xFFFFu) * sc;
       const float dm = f16_bits_to_f32(w.meta.x >> 16) * m;
       acc = fmaf(ds, qa, acc);
