@@ -101,33 +101,62 @@ struct Raw<QMV_Q4K> { uint4 q; uint4 meta; };
 template <>
 struct Raw<QMV_Q6K> { uint4 q; uint2 qh; uint32_t s2; uint32_t d; };
 
-struct Geo {  // plane bases and row strides
-  const uint8_t* W;
-  int64_t off1, off2, off3;
+// Weight planes are read through raw buffer resources: an offset at or past
+// the plane size returns zeros without touching memory.  Rows past N and row
+// groups past the end of a wave's work therefore load unconditionally, so every
+// wave issues the same number of loads in the same order and the compiler's
+// wait counts stay exact (behind a branch it must assume the fewest loads were
+// issued and waits for the newest one).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOOB = 0x80000000u;  // past every plane (planes are < 2^31 bytes)
+constexpr int kRsrcWord3 = 0x00020000;   // raw (untyped) 32-bit data, gfx9 family
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes), kRsrcWord3);
+}
+
+// cache policy of the weight-code loads: non-temporal (read once), like ld_w4
+constexpr int kNT = QMV_NT_WEIGHTS ? 2 : 0;
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+template <int POL>
+__device__ __forceinline__ uint4 bl128(rsrc_t r, uint32_t o) {
+  const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, int(o), 0, POL);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+template <int POL>
+__device__ __forceinline__ uint2 bl64(rsrc_t r, uint32_t o) {
+  const v2u v = __builtin_amdgcn_raw_buffer_load_b64(r, int(o), 0, POL);
+  return make_uint2(v.x, v.y);
+}
+
+struct Geo {  // buffer resources of the planes
+  rsrc_t q, p1, p2, p3;
   int K;
 };
 
+// Unit u (32 weights) of `row`; ok = false reads nothing and yields zeros.
 template <int FMT>
-__device__ __forceinline__ Raw<FMT> load_raw(const Geo& g, int row, int u) {
+__device__ __forceinline__ Raw<FMT> load_raw(const Geo& g, int row, int u, bool ok) {
   Raw<FMT> r;
-  const int64_t R = row;
-  const int K = g.K;
+  const uint32_t R = uint32_t(row), K = uint32_t(g.K), U = uint32_t(u);
+  const uint32_t bad = ok ? 0u : kOOB;
   if constexpr (FMT == QMV_Q8_0) {
-    const uint4* p = reinterpret_cast<const uint4*>(g.W + R * K) + 2 * u;
-    r.q0 = ld_w4(p);
-    r.q1 = ld_w4(p + 1);
-    r.sc = reinterpret_cast<const uint16_t*>(g.W + g.off1)[R * (K >> 5) + u];
+    const uint32_t o = (R * K + 32u * U) | bad;
+    r.q0 = bl128<kNT>(g.q, o);
+    r.q1 = bl128<kNT>(g.q, o + 16u);
+    r.sc = __builtin_amdgcn_raw_buffer_load_b16(g.p1, int(((R * (K >> 5) + U) * 2u) | bad), 0, 0);
   } else if constexpr (FMT == QMV_W4A16_G64) {
-    r.q = ld_w4(reinterpret_cast<const uint4*>(g.W + R * (K >> 1)) + u);
-    r.sz = reinterpret_cast<const uint32_t*>(g.W + g.off1)[R * (K >> 6) + (u >> 1)];
+    r.q = bl128<kNT>(g.q, (R * (K >> 1) + 16u * U) | bad);
+    r.sz = __builtin_amdgcn_raw_buffer_load_b32(g.p1, int(((R * (K >> 6) + (U >> 1)) * 4u) | bad), 0, 0);
   } else if constexpr (FMT == QMV_Q4K) {
-    r.q = ld_w4(reinterpret_cast<const uint4*>(g.W + R * (K >> 1)) + u);
-    r.meta = reinterpret_cast<const uint4*>(g.W + g.off1)[R * (K >> 8) + (u >> 3)];
+    r.q = bl128<kNT>(g.q, (R * (K >> 1) + 16u * U) | bad);
+    r.meta = bl128<0>(g.p1, ((R * (K >> 8) + (U >> 3)) * 16u) | bad);
   } else {
-    r.q = ld_w4(reinterpret_cast<const uint4*>(g.W + R * (K >> 1)) + u);
-    r.qh = ld_w2(reinterpret_cast<const uint2*>(g.W + g.off1) + R * (K >> 5) + u);
-    r.s2 = reinterpret_cast<const uint16_t*>(g.W + g.off2)[R * (K >> 5) + u];
-    r.d = reinterpret_cast<const uint16_t*>(g.W + g.off3)[R * (K >> 8) + (u >> 3)];
+    r.q = bl128<kNT>(g.q, (R * (K >> 1) + 16u * U) | bad);
+    r.qh = bl64<kNT>(g.p1, ((R * (K >> 5) + U) * 8u) | bad);
+    r.s2 = __builtin_amdgcn_raw_buffer_load_b16(g.p2, int(((R * (K >> 5) + U) * 2u) | bad), 0, 0);
+    r.d = __builtin_amdgcn_raw_buffer_load_b16(g.p3, int(((R * (K >> 8) + (U >> 3)) * 2u) | bad), 0, 0);
   }
   return r;
 }
@@ -140,16 +169,28 @@ struct XUnit<false> { float v[32]; float s0, s1; };   // s0: sum of all 32 (or f
 template <>
 struct XUnit<true> { half2_t p[16]; float s; };       // pairs (x_{8i+j}, x_{8i+j+4}), sum
 
+// fp16 activations of one unit (32 values, 4 x 16 bytes), fetched from global
+// memory before the weight loads are issued.
+struct XRaw16 { uint4 v[4]; };
+__device__ __forceinline__ XRaw16 fetch_x16(const void* xv, int64_t off) {
+  const uint4* xp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(xv) + off);
+  XRaw16 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r.v[i] = xp[i];
+  return r;
+}
+
+// fp16 x: from the fetched words `raw`; f32 x: from the block's LDS copy `xv`
+// at float offset `off`.  valid = false gives a zero slice.
 template <int FMT, bool XF16>
 __device__ __forceinline__ void load_x(XUnit<FMT == QMV_W4A16_G64 && XF16>& xu, const void* xv, int64_t off,
-                                       bool valid) {
+                                       bool valid, const XRaw16* raw) {
   if constexpr (FMT == QMV_W4A16_G64 && XF16) {
-    const uint4* xp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(xv) + off);
     float s = 0.0f;
     const half2_t one2 = as_h2(0x3C003C00u);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint4 xx = valid ? xp[i] : make_uint4(0, 0, 0, 0);
+      const uint4 xx = valid ? raw->v[i] : make_uint4(0, 0, 0, 0);
       xu.p[4 * i + 0] = as_h2(__builtin_amdgcn_perm(xx.z, xx.x, 0x05040100u));
       xu.p[4 * i + 1] = as_h2(__builtin_amdgcn_perm(xx.z, xx.x, 0x07060302u));
       xu.p[4 * i + 2] = as_h2(__builtin_amdgcn_perm(xx.w, xx.y, 0x05040100u));
@@ -159,10 +200,9 @@ __device__ __forceinline__ void load_x(XUnit<FMT == QMV_W4A16_G64 && XF16>& xu, 
     }
     xu.s = s;
   } else if constexpr (XF16) {
-    const uint4* xp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(xv) + off);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint4 xx = valid ? xp[i] : make_uint4(0, 0, 0, 0);
+      const uint4 xx = valid ? raw->v[i] : make_uint4(0, 0, 0, 0);
       const uint32_t w[4] = {xx.x, xx.y, xx.z, xx.w};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -288,6 +328,7 @@ struct Seg {
   int b0;   // first block of this segment
   int nb;   // blocks of this segment
   int fmt;  // format (read by the mixed Q4K / Q6K kernel only)
+  uint32_t nrec[4];  // bytes of each plane (buffer-resource ranges; each < 2^31)
 };
 constexpr int kMix = 0;  // FMT of a table mixing Q4K and Q6K segments
 struct SegTable {
@@ -304,18 +345,30 @@ struct SegTable {
 // slice order); ONE: the table holds one segment (its fields then load at
 // fixed offsets, with no scan in front of them).
 // This block's share of one segment (the body of the kernels below).
+// Workgroup barrier for LDS traffic only: __syncthreads() would also wait for
+// every weight load in flight.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// y[row] = v when ok; otherwise the store writes nothing (out-of-range offset),
+// so every lane issues it and the wait counts stay exact.
+__device__ __forceinline__ void store_y(rsrc_t ry, int row, bool ok, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ry, int(ok ? uint32_t(row) * 4u : kOOB), 0, 0);
+}
+
 template <int FMT, bool XF16, int LPR, int UPL, int R, int KS>
 __device__ __forceinline__ void xs_segment(const Seg& sg, const int K) {
   constexpr int TPB = KS == 1 ? kWaves : 1;  // independent lane-group teams per block
+  constexpr int BT = 64 * (KS == 1 ? kWaves : KS);  // threads per block
   constexpr bool H2 = (FMT == QMV_W4A16_G64 && XF16);
   constexpr int RPW = 64 / LPR;
   const int lane = threadIdx.x & 63;
   const int sub = lane / LPR;
   const int l = lane % LPR;
   const int U = K >> 5;
-  const Geo g{sg.W, sg.off1, sg.off2, sg.off3, K};
+  const Geo g{make_rsrc(sg.W, sg.nrec[0]), make_rsrc(sg.W + sg.off1, sg.nrec[1]),
+              make_rsrc(sg.W + sg.off2, sg.nrec[2]), make_rsrc(sg.W + sg.off3, sg.nrec[3]), K};
   const int N = sg.N;
-  float* __restrict__ y = sg.y;
+  const rsrc_t ry = make_rsrc(sg.y, uint32_t(N) * 4u);
   const int ngroups = (N + R * RPW - 1) / (R * RPW);
   // wave-uniform (readfirstlane): the loop's branches and loads stay scalar-controlled
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -335,35 +388,59 @@ __device__ __forceinline__ void xs_segment(const Seg& sg, const int K) {
     sh[j] = 6 * (uu[j] & 7);
   }
 
+  // 1. activations first: with f32 x the block copies the whole vector into LDS
+  // (every wave of the block reads the same vector, so this keeps the 128 bytes
+  // per lane and unit off the vector-memory path); with fp16 x each lane
+  // fetches its own slice
+  constexpr int XF = 32 * LPR * UPL * KS;         // floats of x this configuration covers
+  constexpr int NXI = (XF / 4 + BT - 1) / BT;     // 16-byte staging loads per thread
+  // staged words in one vector value (a private array here was placed in LDS
+  // by the compiler, which waited for each load before the weights went out)
+  typedef float xstage_t __attribute__((ext_vector_type(XF16 ? 4 : 4 * NXI)));
+  [[maybe_unused]] xstage_t xst;
+  [[maybe_unused]] XRaw16 xr[XF16 ? UPL : 1];
+  if constexpr (!XF16) {
+    const float4* xg = static_cast<const float4*>(sg.x);
+    const int n4 = K >> 2;
+#pragma unroll
+    for (int i = 0; i < NXI; ++i) {
+      const float4 t = xg[min(int(threadIdx.x) + i * BT, n4 - 1)];
+      xst[4 * i] = t.x; xst[4 * i + 1] = t.y; xst[4 * i + 2] = t.z; xst[4 * i + 3] = t.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < UPL; ++j) xr[j] = fetch_x16(sg.x, 32 * uu[j]);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the weight loads
+
+  // 2. weights of this wave's first two row groups: both register sets in
+  // flight before anything waits (groups past the end read nothing)
   Raw<FMT> ga[R][UPL], gb[R][UPL];  // two register sets, used in turn (no copies)
   auto load_group = [&](Raw<FMT> (&dst)[R][UPL], int gi) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int row = min(gi * (R * RPW) + r * RPW + sub, N - 1);
+      const int row = gi * (R * RPW) + r * RPW + sub;
 #pragma unroll
-      for (int j = 0; j < UPL; ++j) dst[r][j] = load_raw<FMT>(g, row, uu[j]);
+      for (int j = 0; j < UPL; ++j) dst[r][j] = load_raw<FMT>(g, row, uu[j], row < N && uv[j]);
     }
   };
   int grp = gw;
-  if (grp < ngroups) load_group(ga, grp);
+  load_group(ga, grp);
+  load_group(gb, grp + TW);
 
+  // 3. activation slices into registers (and the per-unit sums)
   XUnit<H2> xs[UPL];
   if constexpr (!XF16) {
-    // f32 activations: every wave of the block reads the same vector, so the
-    // block copies it into LDS once (coalesced 16-byte loads) and each lane
-    // takes its slice from there, which keeps the 128 bytes per lane and unit
-    // off the vector-memory path (measured on MI355X: Q4K 5632 x 2048 6.17 ->
-    // 5.18 us, the 32000 x 2048 Q6K head 15.2 -> 13.8 us)
-    constexpr int XF = 32 * LPR * UPL * KS;  // floats of x this configuration covers
-    __shared__ float4 xl[XF / 4];
-    const float4* xg = static_cast<const float4*>(sg.x);
-    for (int i = threadIdx.x; i < (K >> 2); i += 64 * (KS == 1 ? kWaves : KS)) xl[i] = xg[i];
-    __syncthreads();
+    __shared__ float4 xl[NXI * BT];  // XF / 4 rounded up to whole staging rounds
 #pragma unroll
-    for (int j = 0; j < UPL; ++j) load_x<FMT, XF16>(xs[j], xl, 32 * uu[j], uv[j]);
+    for (int i = 0; i < NXI; ++i)  // unconditional: no load sinks into a branch
+      xl[int(threadIdx.x) + i * BT] = make_float4(xst[4 * i], xst[4 * i + 1], xst[4 * i + 2], xst[4 * i + 3]);
+    lds_barrier();
+#pragma unroll
+    for (int j = 0; j < UPL; ++j) load_x<FMT, XF16>(xs[j], xl, 32 * uu[j], uv[j], nullptr);
   } else {
 #pragma unroll
-    for (int j = 0; j < UPL; ++j) load_x<FMT, XF16>(xs[j], sg.x, 32 * uu[j], uv[j]);
+    for (int j = 0; j < UPL; ++j) load_x<FMT, XF16>(xs[j], nullptr, 0, uv[j], &xr[j]);
   }
 
   auto do_group = [&](const Raw<FMT> (&cur)[R][UPL], int gi) {
@@ -382,36 +459,33 @@ __device__ __forceinline__ void xs_segment(const Seg& sg, const int K) {
       const float tot = group_sum<LPR>(acc[r], sub);
       const int row = gi * (R * RPW) + r * RPW + sub;
       if constexpr (KS == 1) {
-        if (l == 0 && row < N) y[row] = tot;
+        store_y(ry, row, l == 0 && row < N, tot);
       } else {
         if (l == 0) red[par][ks][r * RPW + sub] = tot;
       }
     }
     if constexpr (KS > 1) {  // every wave of the block runs the same groups: uniform barrier
-      __syncthreads();
-      if (ks == 0 && l == 0) {
+      lds_barrier();
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const int row = gi * (R * RPW) + r * RPW + sub;
-          float t = 0.0f;
+      for (int r = 0; r < R; ++r) {
+        const int row = gi * (R * RPW) + r * RPW + sub;
+        float t = 0.0f;
 #pragma unroll
-          for (int w = 0; w < KS; ++w) t += red[par][w][r * RPW + sub];
-          if (row < N) y[row] = t;
-        }
+        for (int w = 0; w < KS; ++w) t += red[par][w][r * RPW + sub];
+        store_y(ry, row, ks == 0 && l == 0 && row < N, t);
       }
       par ^= 1;  // the next group writes the other buffer while this one is read
     }
   };
-  // the next group's loads are in flight while the current one is reduced
+  // a set is refilled as soon as it has been used, so the other set's loads
+  // are always in flight while one group is computed
   while (grp < ngroups) {
-    const int g1 = grp + TW;
-    if (g1 < ngroups) load_group(gb, g1);
     do_group(ga, grp);
-    if (g1 >= ngroups) break;
-    const int g2 = g1 + TW;
-    if (g2 < ngroups) load_group(ga, g2);
-    do_group(gb, g1);
-    grp = g2;
+    load_group(ga, grp + 2 * TW);
+    if (grp + TW >= ngroups) break;
+    do_group(gb, grp + TW);
+    load_group(gb, grp + 3 * TW);
+    grp += 2 * TW;
   }
 }
 
@@ -560,18 +634,35 @@ bool launch_table(int fmt, SegTable& t, int x_dtype, hipStream_t s, hipError_t* 
   }
 }
 
+// The kernels address each plane with 32-bit buffer offsets and use offsets
+// from 2^31 up as "read nothing": every plane must stay below 2^31 bytes.
+bool planes_fit(const Planes& p) {
+  for (int i = 0; i < p.count; ++i)
+    if (p.bytes[i] >= (int64_t(1) << 31)) return false;
+  return true;
+}
+
+Seg make_seg(int fmt, int64_t N, int64_t K, const void* W, const void* x, void* y) {
+  const Planes p = planes_of(fmt, N, K);
+  Seg sg{static_cast<const uint8_t*>(W), p.off[1], p.off[2], p.off[3], x, static_cast<float*>(y), int(N), 0, 0, fmt,
+         {0, 0, 0, 0}};
+  for (int i = 0; i < p.count; ++i) sg.nrec[i] = uint32_t(p.bytes[i]);
+  return sg;
+}
+
 }  // namespace
 
 // Single-vector matvec on the activation-stationary kernels.  Returns false
 // (nothing launched) when the shape needs more activation registers than
-// these kernels hold; the caller then uses the general kernel.
+// these kernels hold, or has a plane of 2^31 bytes or more; the caller then
+// uses the general kernel.
 bool launch_matvec_b1(int fmt, int64_t N, int64_t K, const uint8_t* W, const void* x, int x_dtype,
                       float* y, hipStream_t s, hipError_t* err) {
-  const Planes p = planes_of(fmt, N, K);
+  if (!planes_fit(planes_of(fmt, N, K))) return false;
   SegTable t{};
   t.count = 1;
   t.K = int(K);
-  t.s[0] = Seg{W, p.off[1], p.off[2], p.off[3], x, y, int(N), 0, 0, fmt};
+  t.s[0] = make_seg(fmt, N, K, W, x, y);
   return launch_table(fmt, t, x_dtype, s, err);
 }
 
@@ -588,6 +679,8 @@ bool launch_matvec_grouped_b1(int fmt, int64_t K, int count, const qmv_matvec_it
   const int upl = (U + lpr - 1) / lpr;
   if (upl > (x_dtype == QMV_F16 ? 4 : 3)) return false;
   auto eff = [&](int i) { return items[i].fmt ? items[i].fmt : fmt; };
+  for (int i = 0; i < count; ++i)  // decided before anything is launched
+    if (!planes_fit(planes_of(eff(i), items[i].N, K))) return false;
   // launches over the items with indices idx[0..n), as tables of format tfmt
   auto run = [&](int tfmt, const int* idx, int n) {
     const int64_t max_rows = int64_t(1) << 30;  // a launch takes up to kMaxSeg items and 2^30 rows
@@ -598,9 +691,7 @@ bool launch_matvec_grouped_b1(int fmt, int64_t K, int count, const qmv_matvec_it
       while (t.count < kMaxSeg && i0 + t.count < n && (t.count == 0 || rows + items[idx[i0 + t.count]].N <= max_rows)) {
         const int i = idx[i0 + t.count];
         const qmv_matvec_item& it = items[i];
-        const Planes p = planes_of(eff(i), it.N, K);
-        t.s[t.count++] = Seg{static_cast<const uint8_t*>(it.W), p.off[1], p.off[2], p.off[3], it.x,
-                             static_cast<float*>(it.y), int(it.N), 0, 0, eff(i)};
+        t.s[t.count++] = make_seg(eff(i), it.N, K, it.W, it.x, it.y);
         rows += it.N;
       }
       if (!launch_table(tfmt, t, x_dtype, s, err)) return false;
