@@ -14,6 +14,7 @@
 //  * Partial sums are reduced across the LPR lanes of a row with DPP moves
 //    inside 16-lane rows and ds_bpermute only across rows.
 #include <algorithm>
+#include <climits>
 #include <cstdlib>
 
 #include "qmv_internal.h"
@@ -21,7 +22,10 @@
 namespace qmv {
 namespace {
 
-constexpr int kWaves = 4;
+#ifndef QMV_XS_WAVES
+#define QMV_XS_WAVES 4
+#endif
+constexpr int kWaves = QMV_XS_WAVES;  // waves per block when each wave walks its own row groups
 constexpr int kThreads = 64 * kWaves;
 
 typedef __attribute__((ext_vector_type(2))) _Float16 half2_t;
@@ -332,6 +336,7 @@ struct Seg {
 };
 constexpr int kMix = 0;  // FMT of a table mixing Q4K and Q6K segments
 struct SegTable {
+  int first[kMaxSeg];  // first block of each segment (INT_MAX past count): one wide scalar load
   Seg s[kMaxSeg];
   int count;
   int K;
@@ -492,9 +497,14 @@ __device__ __forceinline__ void xs_segment(const Seg& sg, const int K) {
 template <int FMT, bool XF16, int LPR, int UPL, int R, bool ONE, int KS>
 __global__ __launch_bounds__(KS == 1 ? kThreads : 64 * KS) void matvec_xs_kernel(const SegTable t) {
   // this block's segment (block-uniform scan of at most kMaxSeg entries)
+  // (unused table entries start at INT_MAX, so this is a count over all
+  // entries, read with one wide scalar load, where a loop to t.count waited
+  // for each entry in turn before the first weight load went out)
   int si = 0;
-  if constexpr (!ONE)
-    for (int i = 1; i < t.count; ++i) si = (int(blockIdx.x) >= t.s[i].b0) ? i : si;
+  if constexpr (!ONE) {
+#pragma unroll
+    for (int i = 1; i < kMaxSeg; ++i) si += int(blockIdx.x) >= t.first[i] ? 1 : 0;
+  }
   xs_segment<FMT, XF16, LPR, UPL, R, KS>(t.s[si], t.K);
 }
 
@@ -503,7 +513,8 @@ __global__ __launch_bounds__(KS == 1 ? kThreads : 64 * KS) void matvec_xs_kernel
 template <int LPR, int UPL, int R, int KS>
 __global__ __launch_bounds__(KS == 1 ? kThreads : 64 * KS) void matvec_xs_mix_kernel(const SegTable t) {
   int si = 0;
-  for (int i = 1; i < t.count; ++i) si = (int(blockIdx.x) >= t.s[i].b0) ? i : si;
+#pragma unroll
+  for (int i = 1; i < kMaxSeg; ++i) si += int(blockIdx.x) >= t.first[i] ? 1 : 0;
   const Seg& sg = t.s[si];
   if (sg.fmt == QMV_Q6K) xs_segment<QMV_Q6K, false, LPR, UPL, R, KS>(sg, t.K);
   else xs_segment<QMV_Q4K, false, LPR, UPL, R, KS>(sg, t.K);
@@ -535,6 +546,7 @@ hipError_t go(SegTable& t, hipStream_t s) {
     t.s[i].nb = int(std::max<int64_t>(1, std::min(need, share)));
     b += t.s[i].nb;
   }
+  for (int i = 0; i < kMaxSeg; ++i) t.first[i] = i < t.count ? t.s[i].b0 : INT_MAX;  // INT_MAX: never selected
   if constexpr (FMT == kMix)
     hipLaunchKernelGGL((matvec_xs_mix_kernel<LPR, UPL, R, KS>), dim3(b), dim3(64 * BW), 0, s, t);
   else if (t.count == 1)
