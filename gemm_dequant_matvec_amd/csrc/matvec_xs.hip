@@ -22,6 +22,9 @@
 namespace qmv {
 namespace {
 
+#ifndef QMV_XS_STAGE16
+#define QMV_XS_STAGE16 0  // fp16 activations also staged once per block in LDS
+#endif
 #ifndef QMV_XS_WAVES
 #define QMV_XS_WAVES 4
 #endif
@@ -360,7 +363,7 @@ __device__ __forceinline__ void store_y(rsrc_t ry, int row, bool ok, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ry, int(ok ? uint32_t(row) * 4u : kOOB), 0, 0);
 }
 
-template <int FMT, bool XF16, int LPR, int UPL, int R, int KS>
+template <int FMT, bool XF16, int LPR, int UPL, int R, int KS, bool DB>
 __device__ __forceinline__ void xs_segment(const Seg& sg, const int K) {
   constexpr int TPB = KS == 1 ? kWaves : 1;  // independent lane-group teams per block
   constexpr int BT = 64 * (KS == 1 ? kWaves : KS);  // threads per block
@@ -393,23 +396,26 @@ __device__ __forceinline__ void xs_segment(const Seg& sg, const int K) {
     sh[j] = 6 * (uu[j] & 7);
   }
 
-  // 1. activations first: with f32 x the block copies the whole vector into LDS
-  // (every wave of the block reads the same vector, so this keeps the 128 bytes
-  // per lane and unit off the vector-memory path); with fp16 x each lane
-  // fetches its own slice
-  constexpr int XF = 32 * LPR * UPL * KS;         // floats of x this configuration covers
-  constexpr int NXI = (XF / 4 + BT - 1) / BT;     // 16-byte staging loads per thread
+  // 1. activations first.  With f32 x (and fp16 x when STAGE16) the block
+  // copies the whole vector into LDS: every wave of the block reads the same
+  // vector, so this keeps the per-lane activation loads (128 bytes per unit
+  // for f32) off the vector-memory path.  Otherwise each lane fetches its own
+  // fp16 slice.
+  constexpr bool STAGE = !XF16 || QMV_XS_STAGE16;
+  constexpr int XF = 32 * LPR * UPL * KS;          // activations this configuration covers
+  constexpr int XW = XF16 ? XF / 8 : XF / 4;       // ... in 16-byte words
+  constexpr int NXI = (XW + BT - 1) / BT;          // staging loads per thread
   // staged words in one vector value (a private array here was placed in LDS
   // by the compiler, which waited for each load before the weights went out)
-  typedef float xstage_t __attribute__((ext_vector_type(XF16 ? 4 : 4 * NXI)));
+  typedef uint32_t xstage_t __attribute__((ext_vector_type(STAGE ? 4 * NXI : 4)));
   [[maybe_unused]] xstage_t xst;
   [[maybe_unused]] XRaw16 xr[XF16 ? UPL : 1];
-  if constexpr (!XF16) {
-    const float4* xg = static_cast<const float4*>(sg.x);
-    const int n4 = K >> 2;
+  if constexpr (STAGE) {
+    const uint4* xg = static_cast<const uint4*>(sg.x);
+    const int nw = XF16 ? (K >> 3) : (K >> 2);
 #pragma unroll
     for (int i = 0; i < NXI; ++i) {
-      const float4 t = xg[min(int(threadIdx.x) + i * BT, n4 - 1)];
+      const uint4 t = xg[min(int(threadIdx.x) + i * BT, nw - 1)];
       xst[4 * i] = t.x; xst[4 * i + 1] = t.y; xst[4 * i + 2] = t.z; xst[4 * i + 3] = t.w;
     }
   } else {
@@ -418,8 +424,9 @@ __device__ __forceinline__ void xs_segment(const Seg& sg, const int K) {
   }
   __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the weight loads
 
-  // 2. weights of this wave's first two row groups: both register sets in
-  // flight before anything waits (groups past the end read nothing)
+  // 2. weights of this wave's first two row groups (one with DB = false):
+  // both register sets in flight before anything waits (groups past the end
+  // read nothing)
   Raw<FMT> ga[R][UPL], gb[R][UPL];  // two register sets, used in turn (no copies)
   auto load_group = [&](Raw<FMT> (&dst)[R][UPL], int gi) {
 #pragma unroll
@@ -431,18 +438,29 @@ __device__ __forceinline__ void xs_segment(const Seg& sg, const int K) {
   };
   int grp = gw;
   load_group(ga, grp);
-  load_group(gb, grp + TW);
+  if constexpr (DB) load_group(gb, grp + TW);
 
   // 3. activation slices into registers (and the per-unit sums)
   XUnit<H2> xs[UPL];
-  if constexpr (!XF16) {
-    __shared__ float4 xl[NXI * BT];  // XF / 4 rounded up to whole staging rounds
+  if constexpr (STAGE) {
+    __shared__ uint4 xl[NXI * BT];  // XW rounded up to whole staging rounds
 #pragma unroll
     for (int i = 0; i < NXI; ++i)  // unconditional: no load sinks into a branch
-      xl[int(threadIdx.x) + i * BT] = make_float4(xst[4 * i], xst[4 * i + 1], xst[4 * i + 2], xst[4 * i + 3]);
+      xl[int(threadIdx.x) + i * BT] = make_uint4(xst[4 * i], xst[4 * i + 1], xst[4 * i + 2], xst[4 * i + 3]);
     lds_barrier();
+    if constexpr (XF16) {
 #pragma unroll
-    for (int j = 0; j < UPL; ++j) load_x<FMT, XF16>(xs[j], xl, 32 * uu[j], uv[j], nullptr);
+      for (int j = 0; j < UPL; ++j) {
+        const uint4* xp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(xl) + 32 * uu[j]);
+        XRaw16 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w.v[i] = xp[i];
+        load_x<FMT, XF16>(xs[j], nullptr, 0, uv[j], &w);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < UPL; ++j) load_x<FMT, XF16>(xs[j], xl, 32 * uu[j], uv[j], nullptr);
+    }
   } else {
 #pragma unroll
     for (int j = 0; j < UPL; ++j) load_x<FMT, XF16>(xs[j], nullptr, 0, uv[j], &xr[j]);
@@ -482,19 +500,25 @@ __device__ __forceinline__ void xs_segment(const Seg& sg, const int K) {
       par ^= 1;  // the next group writes the other buffer while this one is read
     }
   };
-  // a set is refilled as soon as it has been used, so the other set's loads
-  // are always in flight while one group is computed
-  while (grp < ngroups) {
-    do_group(ga, grp);
-    load_group(ga, grp + 2 * TW);
-    if (grp + TW >= ngroups) break;
-    do_group(gb, grp + TW);
-    load_group(gb, grp + 3 * TW);
-    grp += 2 * TW;
+  if constexpr (DB) {
+    // a set is refilled as soon as it has been used, so the other set's loads
+    // are always in flight while one group is computed
+    while (grp < ngroups) {
+      do_group(ga, grp);
+      load_group(ga, grp + 2 * TW);
+      if (grp + TW >= ngroups) break;
+      do_group(gb, grp + TW);
+      load_group(gb, grp + 3 * TW);
+      grp += 2 * TW;
+    }
+  } else {  // at most one group per wave (the launcher checks)
+    if (grp < ngroups) do_group(ga, grp);
   }
 }
 
-template <int FMT, bool XF16, int LPR, int UPL, int R, bool ONE, int KS>
+// DB: each wave may take several row groups (two register sets in turn);
+// false when every wave has at most one.
+template <int FMT, bool XF16, int LPR, int UPL, int R, bool ONE, int KS, bool DB>
 __global__ __launch_bounds__(KS == 1 ? kThreads : 64 * KS) void matvec_xs_kernel(const SegTable t) {
   // this block's segment (block-uniform scan of at most kMaxSeg entries)
   // (unused table entries start at INT_MAX, so this is a count over all
@@ -505,19 +529,27 @@ __global__ __launch_bounds__(KS == 1 ? kThreads : 64 * KS) void matvec_xs_kernel
 #pragma unroll
     for (int i = 1; i < kMaxSeg; ++i) si += int(blockIdx.x) >= t.first[i] ? 1 : 0;
   }
-  xs_segment<FMT, XF16, LPR, UPL, R, KS>(t.s[si], t.K);
+  xs_segment<FMT, XF16, LPR, UPL, R, KS, DB>(t.s[si], t.K);
 }
 
 // Q4K and Q6K segments in one launch (the K-quant mix of one decoder layer's
 // q / k / v projections): each block takes its own segment's format path.
-template <int LPR, int UPL, int R, int KS>
+template <int LPR, int UPL, int R, int KS, bool DB>
 __global__ __launch_bounds__(KS == 1 ? kThreads : 64 * KS) void matvec_xs_mix_kernel(const SegTable t) {
   int si = 0;
 #pragma unroll
   for (int i = 1; i < kMaxSeg; ++i) si += int(blockIdx.x) >= t.first[i] ? 1 : 0;
   const Seg& sg = t.s[si];
-  if (sg.fmt == QMV_Q6K) xs_segment<QMV_Q6K, false, LPR, UPL, R, KS>(sg, t.K);
-  else xs_segment<QMV_Q4K, false, LPR, UPL, R, KS>(sg, t.K);
+  if (sg.fmt == QMV_Q6K) xs_segment<QMV_Q6K, false, LPR, UPL, R, KS, DB>(sg, t.K);
+  else xs_segment<QMV_Q4K, false, LPR, UPL, R, KS, DB>(sg, t.K);
+}
+
+bool double_buffer_forced() {
+  static const bool v = [] {
+    const char* e = getenv("QMV_MATVEC_DB");  // A/B tuning only: 1 keeps both register sets always
+    return e && atoi(e) == 1;
+  }();
+  return v;
 }
 
 template <int FMT, bool XF16, int LPR, int UPL, int R, int KS>
@@ -547,12 +579,20 @@ hipError_t go(SegTable& t, hipStream_t s) {
     b += t.s[i].nb;
   }
   for (int i = 0; i < kMaxSeg; ++i) t.first[i] = i < t.count ? t.s[i].b0 : INT_MAX;  // INT_MAX: never selected
-  if constexpr (FMT == kMix)
-    hipLaunchKernelGGL((matvec_xs_mix_kernel<LPR, UPL, R, KS>), dim3(b), dim3(64 * BW), 0, s, t);
-  else if (t.count == 1)
-    hipLaunchKernelGGL((matvec_xs_kernel<FMT, XF16, LPR, UPL, R, true, KS>), dim3(b), dim3(64 * BW), 0, s, t);
-  else
-    hipLaunchKernelGGL((matvec_xs_kernel<FMT, XF16, LPR, UPL, R, false, KS>), dim3(b), dim3(64 * BW), 0, s, t);
+  // one row group per team everywhere: no second register set (its loads would
+  // all fall past the end)
+  bool single = !double_buffer_forced();
+  for (int i = 0; i < t.count; ++i) single = single && groups[i] <= int64_t(t.s[i].nb) * TPB;
+  const dim3 grid(b), block(64 * BW);
+  if (single) {
+    if constexpr (FMT == kMix) hipLaunchKernelGGL((matvec_xs_mix_kernel<LPR, UPL, R, KS, false>), grid, block, 0, s, t);
+    else if (t.count == 1) hipLaunchKernelGGL((matvec_xs_kernel<FMT, XF16, LPR, UPL, R, true, KS, false>), grid, block, 0, s, t);
+    else hipLaunchKernelGGL((matvec_xs_kernel<FMT, XF16, LPR, UPL, R, false, KS, false>), grid, block, 0, s, t);
+  } else {
+    if constexpr (FMT == kMix) hipLaunchKernelGGL((matvec_xs_mix_kernel<LPR, UPL, R, KS, true>), grid, block, 0, s, t);
+    else if (t.count == 1) hipLaunchKernelGGL((matvec_xs_kernel<FMT, XF16, LPR, UPL, R, true, KS, true>), grid, block, 0, s, t);
+    else hipLaunchKernelGGL((matvec_xs_kernel<FMT, XF16, LPR, UPL, R, false, KS, true>), grid, block, 0, s, t);
+  }
   return hipGetLastError();
 }
 
