@@ -596,18 +596,26 @@ hipError_t go(SegTable& t, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Rows per lane group, from measurements on MI355X over twelve shapes (all
-// formats, K = 512 to 5632, 256 to 151936 rows, R = 1, 2, 4): one row when the
-// launch has at most 1024 row slots (rows / rows read side by side per wave:
-// the launch is latency-bound and waves count), else two (twice the loads in
-// flight per wave, half the activation reloads), four for Q6K from 16384 slots
-// (the 32000 x 2048 head: 5 % faster than two).
+// Rows per lane group R.  One row when the launch has at most 1024 row slots
+// (rows / rows read side by side per wave): the launch is latency-bound and
+// waves count.  Otherwise two, or four with fp16 W4A16 activations and K in
+// one wave, measured on MI355X with the static load schedule (grouped
+// 2 x 5632 x 2048 W4A16 gate+up: R = 1 / 2 / 4: 5.82 / 5.89 / 5.48 us; the
+// K-split 2048 x 5632 down: 4.38 / 4.10 / 4.36 us; the 32000 x 2048 Q6K head
+// and the 151936 x 1024 Q4K head are best at two).  R = 8 (fp16 W4A16, K in
+// one wave) only through the tuning switch.
 template <int FMT, bool XF16, int LPR, int UPL, int KS = 1>
 hipError_t pick_r(SegTable& t, int rsel, hipStream_t s) {
+  constexpr bool H2 = (FMT == QMV_W4A16_G64 && XF16);
   int64_t rows = 0;
   for (int i = 0; i < t.count; ++i) rows += t.s[i].N;
   const int64_t slots = rows / (64 / LPR);
-  const int r = rsel ? rsel : slots <= 1024 ? 1 : (FMT == QMV_Q6K && slots >= 16384) ? 4 : 2;
+  int r = rsel ? rsel : slots <= 1024 ? 1 : (H2 && KS == 1) ? 4 : 2;
+  if constexpr (H2 && KS == 1) {
+    if (r == 8) return go<FMT, XF16, LPR, UPL, 8, KS>(t, s);
+  } else {
+    r = r == 8 ? 4 : r;
+  }
   if (r == 4) return go<FMT, XF16, LPR, UPL, 4, KS>(t, s);
   return r == 2 ? go<FMT, XF16, LPR, UPL, 2, KS>(t, s) : go<FMT, XF16, LPR, UPL, 1, KS>(t, s);
 }
@@ -665,9 +673,9 @@ bool dispatch(SegTable& t, int rsel, hipStream_t s, hipError_t* e) {
 
 int rows_override() {
   static const int v = [] {
-    const char* e = getenv("QMV_MATVEC_ROWS");  // A/B tuning only: rows per lane group (1, 2 or 4)
+    const char* e = getenv("QMV_MATVEC_ROWS");  // A/B tuning only: rows per lane group (1, 2, 4 or 8)
     const int r = e ? atoi(e) : 0;
-    return (r == 1 || r == 2 || r == 4) ? r : 0;
+    return (r == 1 || r == 2 || r == 4 || r == 8) ? r : 0;
   }();
   return v;
 }
