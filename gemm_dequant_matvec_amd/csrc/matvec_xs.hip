@@ -95,6 +95,46 @@ __device__ __forceinline__ float group_sum(float v, int sub) {
   }
 }
 
+// gfx950 cross-half swaps, written out: the compiler builtins returned the first
+// register for both results in this toolchain.  Each is a register permute
+// with both operands read and written; the s_nop pairs give the wait states
+// around a VALU write / read of the operands.
+__device__ __forceinline__ void swap32(float& a, float& b) {  // a.hi <-> b.lo (32-lane halves)
+  asm("s_nop 4\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 4" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap16(float& a, float& b) {  // odd 16-lane rows of a <-> even rows of b
+  asm("s_nop 4\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 4" : "+v"(a), "+v"(b));
+}
+
+// Totals of acc[0 .. R) over all 64 lanes (R rows, each spread over the whole
+// wave): afterwards every lane l holds the total of row l / (64 / R).  The
+// swaps fold the rows into disjoint lane ranges, so R rows cost 2R - 1
+// swaps-and-adds plus one 16-lane DPP sum (R = 4: ~12 instructions, where a
+// DPP sum and four readlanes per row took ~44).
+template <int R>
+__device__ __forceinline__ float wave_rows_sum(const float (&acc)[R]) {
+  if constexpr (R == 4) {
+    float a0 = acc[0], a1 = acc[1], a2 = acc[2], a3 = acc[3];
+    swap32(a0, a2);  // a0 = [row 0 low half, row 2 low half], a2 = [row 0 high half, row 2 high half]
+    swap32(a1, a3);
+    float s02 = a0 + a2, s13 = a1 + a3;  // 32-lane partials: rows 0 | 2 and 1 | 3
+    swap16(s02, s13);
+    return row16_sum(s02 + s13);         // 16-lane row j: row j
+  } else if constexpr (R == 2) {
+    float a0 = acc[0], a1 = acc[1];
+    swap32(a0, a1);
+    float s = a0 + a1, t = s;            // lanes 0-31: row 0, 32-63: row 1
+    swap16(s, t);
+    return row16_sum(s + t);
+  } else {
+    float a = acc[0], b = acc[0];
+    swap32(a, b);
+    float s = a + b, t = s;
+    swap16(s, t);
+    return row16_sum(s + t);
+  }
+}
+
 // ----------------------------------------------------------- per-format units
 
 template <int FMT>
@@ -483,14 +523,27 @@ __device__ __forceinline__ void xs_segment(const Seg& sg, const int K) {
         for (int r = 0; r < R; ++r) acc[r] = unit_dot<FMT, XF16>(cur[r][j], xs[j], sh[j], acc[r]);
       }
     }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float tot = group_sum<LPR>(acc[r], sub);
-      const int row = gi * (R * RPW) + r * RPW + sub;
+    if constexpr (LPR == 64 && (R == 1 || R == 2 || R == 4)) {
+      // one row per lane range: lane l holds row r = l / (64 / R)
+      const float tot = wave_rows_sum<R>(acc);
+      const int r = lane / (64 / R);
+      const bool first = lane % (64 / R) == 0;
+      const int row = gi * R + r;
       if constexpr (KS == 1) {
-        store_y(ry, row, l == 0 && row < N, tot);
+        store_y(ry, row, first && row < N, tot);
       } else {
-        if (l == 0) red[par][ks][r * RPW + sub] = tot;
+        if (first) red[par][ks][r] = tot;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float tot = group_sum<LPR>(acc[r], sub);
+        const int row = gi * (R * RPW) + r * RPW + sub;
+        if constexpr (KS == 1) {
+          store_y(ry, row, l == 0 && row < N, tot);
+        } else {
+          if (l == 0) red[par][ks][r * RPW + sub] = tot;
+        }
       }
     }
     if constexpr (KS > 1) {  // every wave of the block runs the same groups: uniform barrier
