@@ -627,7 +627,13 @@ hipError_t go(SegTable& t, hipStream_t s) {
   // take two groups; the f32-activation paths and the large heads ran slower
   // with more waves).
   constexpr bool H2 = (FMT == QMV_W4A16_G64 && XF16);
-  const int64_t max_blocks = 256 * ((H2 && total * KS <= 256 * 24) ? 24 : 16) / BW;
+  static const int waves_forced = [] {  // A/B tuning only: waves per CU the grid may fill
+    const char* e = getenv("QMV_MATVEC_WAVES_CU");
+    const int v = e ? atoi(e) : 0;
+    return (v >= 4 && v <= 32) ? v : 0;
+  }();
+  const int64_t max_blocks =
+      256 * (waves_forced ? waves_forced : (H2 && total * KS <= 256 * 24) ? 24 : 16) / BW;
   const int64_t budget = std::min<int64_t>((total + TPB - 1) / TPB, max_blocks);
   int b = 0;
   for (int i = 0; i < t.count; ++i) {
