@@ -290,3 +290,41 @@ def test_config_decode_sweep_layer_and_head(qmv, batch):
         r, _, _ = check_matvec(qmv, fmt, w, x, "f32", rows=rows)
         _say(name, batch, r)
         assert r["ok"], (name, r)
+
+
+def test_matvec_code_plane_past_2gib(qmv):
+    """A Q8_0 matrix whose code plane is past 2 GiB (N * K = 2^31 + 48 K bytes).
+
+    The batch-1 kernels address a plane with 32-bit offsets and reserve
+    offsets from 2^31 up for "read nothing", so they hand such a matrix to the
+    general kernel, as the matrix-core kernel does for batch 2.  Sampled rows
+    (first, last, a random spread) at batch 1 and 2 and through a grouped call
+    with a small matrix beside it match the oracle."""
+    fmt, K = "q8_0", 4096
+    N = (1 << 31) // K + 48
+    w = wl.gen_weights(fmt, N, K, (0, 0, 9))
+    Wp = pack_dev(qmv, fmt, w)
+    rows = np.unique(np.concatenate([_sample_rows(N, 256, seed=3), np.arange(N - 64, N)]))
+    W32 = oracle.dequant_rows(fmt, w, rows)
+    del w
+    for batch in (1, 2):
+        x = wl.gen_x(K, batch, "f32", (0, 0, 9))
+        y = qmv.matvec(fmt, Wp, dev_x(x, "f32"), N, K)
+        torch.cuda.synchronize()
+        xv = x_values(x, "f32")
+        r = oracle.check_within(y.cpu().numpy()[:, rows], oracle.matvec_ref(W32, xv),
+                                oracle.tolerance_bound(W32, xv, oracle.reference.TAU_F32))
+        _say("q8_0 plane past 2 GiB", batch, r)
+        assert r["ok"], (batch, r)
+    # grouped, batch 1: the big matrix beside a small one sharing x
+    ws = wl.gen_weights(fmt, 96, K, (0, 1, 9))
+    Ws = pack_dev(qmv, fmt, ws)
+    x = wl.gen_x(K, 1, "f32", (0, 0, 9))
+    xd = dev_x(x, "f32")
+    yb, ys = qmv.matvec_grouped(fmt, [(Wp, xd, N), (Ws, xd, 96)], K)
+    torch.cuda.synchronize()
+    xv = x_values(x, "f32")
+    for y, W, rr in ((yb, W32, rows), (ys, oracle.dequant_rows(fmt, ws, np.arange(96)), np.arange(96))):
+        r = oracle.check_within(y.cpu().numpy()[:, rr], oracle.matvec_ref(W, xv),
+                                oracle.tolerance_bound(W, xv, oracle.reference.TAU_F32))
+        assert r["ok"], r
