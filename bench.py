@@ -273,6 +273,48 @@ def copy_probe():
     return {"bytes": 2 * n, "gbs": 2 * n / (ms * 1e-3) / 1e9, "what": "torch copy_ of 1 GiB (read+write)"}
 
 
+def platform_probes(qmv):
+    """The machine's own ceilings, for reading the other figures: device-copy GB/s
+    (read + write) at 16 MiB .. 4 GiB (past the 256 MB Infinity Cache from 256 MiB
+    up), and the cost of one tiny kernel launch, eager and inside a HIP graph."""
+    import torch
+    out = {"copy_gbs": {}}
+    for mib in (16, 64, 256, 1024, 4096):
+        n = mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        reps = 20 if mib <= 256 else 5
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            b.copy_(a)
+        t1.record()
+        t1.synchronize()
+        ms = t0.elapsed_time(t1) / reps
+        out["copy_gbs"][f"{mib}MiB"] = 2 * n / (ms * 1e-3) / 1e9
+        del a, b
+    z = torch.zeros(1, device="cuda")
+    n_launch = 200
+
+    def tiny():
+        for _ in range(n_launch):
+            z.fill_(1.0)
+    tiny()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    tiny()
+    t1.record()
+    t1.synchronize()
+    out["launch_us_eager"] = t0.elapsed_time(t1) * 1e3 / n_launch
+    ms, _ = time_graph(tiny, 10, 3)
+    out["launch_us_graph"] = ms * 1e3 / n_launch
+    out["what"] = "torch copy_ per size; launch: one-element fill kernel, 200 back to back"
+    return out
+
+
 def leg_q8_0(qmv):
     """Q8_0 512x512: one launch, latency-bound (same matrix 20x back to back)."""
     import workloads as wl
@@ -312,6 +354,7 @@ def leg_sweep(qmv, b):
 
 
 LEGS = {
+    "platform_probes": platform_probes,
     "q8_0_512x512_b1_single": leg_q8_0,
     "q4k_0.6B_mlp_b1_cold": leg_mlp06,
     "q4k_vocab_head_151936x1024_b1_cold": leg_head06,
