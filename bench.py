@@ -233,9 +233,9 @@ def kernel_leg(qmv, st, steps, warmup):
 # Source files of the matvec kernels the headline launches, and the kernel
 # instantiation the dispatcher picks for the grouped gate / up launch (fp16 x,
 # K = 2048: 64 lanes per row, one unit per lane, four rows per lane group, two
-# segments, K not split, one row group per wave).
+# segments in a 4-entry table, K not split, one row group per wave).
 MATVEC_SOURCES = ["gemm_dequant_matvec_amd/csrc/matvec_xs.hip", "gemm_dequant_matvec_amd/csrc/qmv_internal.h"]
-GATE_KERNEL = "matvec_xs_kernel<2, true, 64, 1, 4, false, 1, false>"
+GATE_KERNEL = "matvec_xs_kernel<2, true, 64, 1, 4, 4, 1, false>"
 
 
 def measured_traffic(profile: str, kernel: str):

@@ -16,6 +16,7 @@
 #include <algorithm>
 #include <climits>
 #include <cstdlib>
+#include <type_traits>
 
 #include "qmv_internal.h"
 
@@ -384,20 +385,38 @@ struct Seg {
   uint32_t nrec[4];  // bytes of each plane (buffer-resource ranges; each < 2^31)
 };
 constexpr int kMix = 0;  // FMT of a table mixing Q4K and Q6K segments
-struct SegTable {
-  int first[kMaxSeg];  // first block of each segment (INT_MAX past count): one wide scalar load
-  Seg s[kMaxSeg];
+// The table is the launch's kernel argument, so its size is paid by every
+// launch: kernels take a table of capacity CAP = 1, 4 or 16, the smallest that
+// holds the launch's segments (MI355X, grouped 2 x 5632 x 2048 gate+up:
+// 5.13 us with a 16-entry table of 1.35 KB, 4.84 us with a 4-entry one).
+template <int CAP>
+struct SegTableT {
+  int first[CAP];  // first block of each segment (INT_MAX past count): one wide scalar load
+  Seg s[CAP];
   int count;
   int K;
 };
+using SegTable = SegTableT<kMaxSeg>;  // built on the host, then shrunk to the launch
+
+template <int CAP>
+SegTableT<CAP> shrink(const SegTable& t) {  // t.count <= CAP
+  SegTableT<CAP> o{};
+  for (int i = 0; i < CAP; ++i) {
+    o.first[i] = t.first[i];
+    o.s[i] = t.s[i];
+  }
+  o.count = t.count;
+  o.K = t.K;
+  return o;
+}
 
 // FMT / XF16: format and activation type; LPR lanes per row; UPL units per lane
 // (covers K = 32 * LPR * UPL * KS, ragged tail masked); R rows per lane group;
 // KS: waves that split K between them (1: every wave walks its own row groups
 // over the whole of K; KS > 1: the KS waves of a block each take one slice
 // of K for the same row groups and their partial sums meet in LDS, added in
-// slice order); ONE: the table holds one segment (its fields then load at
-// fixed offsets, with no scan in front of them).
+// slice order); CAP: table capacity (1: the fields load at fixed offsets,
+// with no scan in front of them).
 // This block's share of one segment (the body of the kernels below).
 // Workgroup barrier for LDS traffic only: __syncthreads() would also wait for
 // every weight load in flight.
@@ -577,27 +596,27 @@ __device__ __forceinline__ void xs_segment(const Seg& sg, const int K) {
 
 // DB: each wave may take several row groups (two register sets in turn);
 // false when every wave has at most one.
-template <int FMT, bool XF16, int LPR, int UPL, int R, bool ONE, int KS, bool DB>
-__global__ __launch_bounds__(KS == 1 ? kThreads : 64 * KS) void matvec_xs_kernel(const SegTable t) {
-  // this block's segment (block-uniform scan of at most kMaxSeg entries)
+template <int FMT, bool XF16, int LPR, int UPL, int R, int CAP, int KS, bool DB>
+__global__ __launch_bounds__(KS == 1 ? kThreads : 64 * KS) void matvec_xs_kernel(const SegTableT<CAP> t) {
+  // this block's segment (block-uniform scan of at most CAP entries)
   // (unused table entries start at INT_MAX, so this is a count over all
   // entries, read with one wide scalar load, where a loop to t.count waited
   // for each entry in turn before the first weight load went out)
   int si = 0;
-  if constexpr (!ONE) {
+  if constexpr (CAP > 1) {
 #pragma unroll
-    for (int i = 1; i < kMaxSeg; ++i) si += int(blockIdx.x) >= t.first[i] ? 1 : 0;
+    for (int i = 1; i < CAP; ++i) si += int(blockIdx.x) >= t.first[i] ? 1 : 0;
   }
   xs_segment<FMT, XF16, LPR, UPL, R, KS, DB>(t.s[si], t.K);
 }
 
 // Q4K and Q6K segments in one launch (the K-quant mix of one decoder layer's
 // q / k / v projections): each block takes its own segment's format path.
-template <int LPR, int UPL, int R, int KS, bool DB>
-__global__ __launch_bounds__(KS == 1 ? kThreads : 64 * KS) void matvec_xs_mix_kernel(const SegTable t) {
+template <int LPR, int UPL, int R, int KS, bool DB, int CAP>
+__global__ __launch_bounds__(KS == 1 ? kThreads : 64 * KS) void matvec_xs_mix_kernel(const SegTableT<CAP> t) {
   int si = 0;
 #pragma unroll
-  for (int i = 1; i < kMaxSeg; ++i) si += int(blockIdx.x) >= t.first[i] ? 1 : 0;
+  for (int i = 1; i < CAP; ++i) si += int(blockIdx.x) >= t.first[i] ? 1 : 0;
   const Seg& sg = t.s[si];
   if (sg.fmt == QMV_Q6K) xs_segment<QMV_Q6K, false, LPR, UPL, R, KS, DB>(sg, t.K);
   else xs_segment<QMV_Q4K, false, LPR, UPL, R, KS, DB>(sg, t.K);
@@ -649,15 +668,24 @@ hipError_t go(SegTable& t, hipStream_t s) {
   bool single = !double_buffer_forced();
   for (int i = 0; i < t.count; ++i) single = single && groups[i] <= int64_t(t.s[i].nb) * TPB;
   const dim3 grid(b), block(64 * BW);
-  if (single) {
-    if constexpr (FMT == kMix) hipLaunchKernelGGL((matvec_xs_mix_kernel<LPR, UPL, R, KS, false>), grid, block, 0, s, t);
-    else if (t.count == 1) hipLaunchKernelGGL((matvec_xs_kernel<FMT, XF16, LPR, UPL, R, true, KS, false>), grid, block, 0, s, t);
-    else hipLaunchKernelGGL((matvec_xs_kernel<FMT, XF16, LPR, UPL, R, false, KS, false>), grid, block, 0, s, t);
-  } else {
-    if constexpr (FMT == kMix) hipLaunchKernelGGL((matvec_xs_mix_kernel<LPR, UPL, R, KS, true>), grid, block, 0, s, t);
-    else if (t.count == 1) hipLaunchKernelGGL((matvec_xs_kernel<FMT, XF16, LPR, UPL, R, true, KS, true>), grid, block, 0, s, t);
-    else hipLaunchKernelGGL((matvec_xs_kernel<FMT, XF16, LPR, UPL, R, false, KS, true>), grid, block, 0, s, t);
-  }
+  auto launch = [&](auto db) {
+    constexpr bool DB = decltype(db)::value;
+    if constexpr (FMT == kMix) {  // a mix has two segments at least
+      if (t.count <= 4)
+        hipLaunchKernelGGL((matvec_xs_mix_kernel<LPR, UPL, R, KS, DB, 4>), grid, block, 0, s, shrink<4>(t));
+      else
+        hipLaunchKernelGGL((matvec_xs_mix_kernel<LPR, UPL, R, KS, DB, kMaxSeg>), grid, block, 0, s, t);
+    } else {
+      if (t.count == 1)
+        hipLaunchKernelGGL((matvec_xs_kernel<FMT, XF16, LPR, UPL, R, 1, KS, DB>), grid, block, 0, s, shrink<1>(t));
+      else if (t.count <= 4)
+        hipLaunchKernelGGL((matvec_xs_kernel<FMT, XF16, LPR, UPL, R, 4, KS, DB>), grid, block, 0, s, shrink<4>(t));
+      else
+        hipLaunchKernelGGL((matvec_xs_kernel<FMT, XF16, LPR, UPL, R, kMaxSeg, KS, DB>), grid, block, 0, s, t);
+    }
+  };
+  if (single) launch(std::false_type{});
+  else launch(std::true_type{});
   return hipGetLastError();
 }
 
@@ -676,7 +704,7 @@ hipError_t pick_r(SegTable& t, int rsel, hipStream_t s) {
   for (int i = 0; i < t.count; ++i) rows += t.s[i].N;
   const int64_t slots = rows / (64 / LPR);
   int r = rsel ? rsel : slots <= 1024 ? 1 : (H2 && KS == 1) ? 4 : 2;
-  if constexpr (H2 && KS == 1) {
+  if constexpr (H2 && KS == 1 && UPL == 1) {
     if (r == 8) return go<FMT, XF16, LPR, UPL, 8, KS>(t, s);
   } else {
     r = r == 8 ? 4 : r;
