@@ -31,6 +31,8 @@
 #include <algorithm>
 #include <cstdlib>
 
+#include <climits>
+
 #include "qmv_internal.h"
 
 namespace qmv {
@@ -72,10 +74,31 @@ struct MSeg {
   int fmt;     // format (read by the mixed Q4K / Q6K kernel only)
 };
 constexpr int kMixM = 0;  // table format of a Q4K / Q6K mix
-struct MTable {
-  MSeg s[kMaxSeg];
+// The table is the kernel argument, so its size is paid by every launch:
+// kernels take a table of capacity CAP = 1, 4 or 16, the smallest that holds
+// the launch's segments (the batch-1 kernels measured ~0.3 us per launch
+// between 16 and 4 entries).
+template <int CAP>
+struct MTableT {
+  int first[CAP];  // first workgroup of each segment (INT_MAX past count): one wide scalar load
+  MSeg s[CAP];
   int count, K, nv, waves;
 };
+using MTable = MTableT<kMaxSeg>;  // built on the host, then shrunk to the launch
+
+template <int CAP>
+MTableT<CAP> shrink(const MTable& t) {  // t.count <= CAP
+  MTableT<CAP> o{};
+  for (int i = 0; i < CAP; ++i) {
+    o.first[i] = t.first[i];
+    o.s[i] = t.s[i];
+  }
+  o.count = t.count;
+  o.K = t.K;
+  o.nv = t.nv;
+  o.waves = t.waves;
+  return o;
+}
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   bf16x2 v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
@@ -382,8 +405,8 @@ struct Staging {
 //
 // One workgroup's share of one segment: stage is the workgroup's staging LDS
 // (SD dwords per wave), red its reduction LDS.
-template <int FMT, bool XF16, int KF, int SD>
-__device__ __forceinline__ void mfma_segment(const MTable& tb, const MSeg& sg, uint32_t* stage, float* red) {
+template <int FMT, bool XF16, int KF, int SD, class TB>
+__device__ __forceinline__ void mfma_segment(const TB& tb, const MSeg& sg, uint32_t* stage, float* red) {
   constexpr int MW = kMaxWaves<KF>;
   const MfmaArgs a{sg.W, sg.off1, sg.off2, sg.off3, sg.x, sg.y, sg.N, tb.K, tb.nv, tb.waves};
   const int bid = int(blockIdx.x) - sg.b0, nblk = sg.nb;
@@ -486,7 +509,7 @@ __device__ __forceinline__ void mfma_segment(const MTable& tb, const MSeg& sg, u
     rb[2 * lane] = acc0;
     rb[2 * lane + 1] = acc1;
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    for (int t = threadIdx.x; t < 128; t += blockDim.x) {
+    for (int t = threadIdx.x; t < 128; t += 64 * a.waves) {  // (blockDim.x: reading it adds ~256 bytes of hidden kernel arguments)
       const int i = t & 15;  // weight row within the tile
       const int v = t >> 4;  // vector
       const int src = 2 * (i + 16 * (v >> 1)) + (v & 1);
@@ -503,16 +526,17 @@ __device__ __forceinline__ void mfma_segment(const MTable& tb, const MSeg& sg, u
 
 // FMT = kMixM: a table of Q4K and Q6K segments, each workgroup taking its
 // segment's format path (a workgroup-uniform branch).
-template <int FMT, bool XF16, int KF>
-__global__ __launch_bounds__(64 * kMaxWaves<KF>) void matvec_mfma_kernel(const MTable tb) {
+template <int FMT, bool XF16, int KF, int CAP>
+__global__ __launch_bounds__(64 * kMaxWaves<KF>) void matvec_mfma_kernel(const MTableT<CAP> tb) {
   constexpr int MW = kMaxWaves<KF>;
   constexpr int SD = FMT == kMixM ? kStageDw<QMV_Q6K> : kStageDw<FMT>;
   static_assert(kStageDw<QMV_Q4K> <= kStageDw<QMV_Q6K>, "mixed staging size");
   __shared__ uint32_t stage_lds[MW * SD];
   __shared__ f32x4 red_raw[2][MW][32];  // [buffer][wave][lane pair] -> 2 x float2
   float* red = reinterpret_cast<float*>(red_raw);
-  int si = 0;  // this workgroup's segment (workgroup-uniform scan)
-  for (int i = 1; i < tb.count; ++i) si = (int(blockIdx.x) >= tb.s[i].b0) ? i : si;
+  int si = 0;  // this workgroup's segment: a count over the first-workgroup array
+#pragma unroll
+  for (int i = 1; i < CAP; ++i) si += int(blockIdx.x) >= tb.first[i] ? 1 : 0;
   const MSeg& sg = tb.s[si];
   if constexpr (FMT == kMixM) {
     if (sg.fmt == QMV_Q6K) mfma_segment<QMV_Q6K, false, KF, SD>(tb, sg, stage_lds, red);
@@ -549,7 +573,14 @@ hipError_t go(MTable& t, hipStream_t s) {
     t.s[i].nb = int(std::max<int64_t>(1, std::min(tiles[i], share)));
     b += t.s[i].nb;
   }
-  hipLaunchKernelGGL((matvec_mfma_kernel<FMT, XF16, KF>), dim3(b), dim3(64 * t.waves), 0, s, t);
+  for (int i = 0; i < kMaxSeg; ++i) t.first[i] = i < t.count ? t.s[i].b0 : INT_MAX;  // INT_MAX: never selected
+  const dim3 grid(b), block(64 * t.waves);
+  if (t.count == 1 && FMT != kMixM)
+    hipLaunchKernelGGL((matvec_mfma_kernel<FMT, XF16, KF, 1>), grid, block, 0, s, shrink<1>(t));
+  else if (t.count <= 4)
+    hipLaunchKernelGGL((matvec_mfma_kernel<FMT, XF16, KF, 4>), grid, block, 0, s, shrink<4>(t));
+  else
+    hipLaunchKernelGGL((matvec_mfma_kernel<FMT, XF16, KF, kMaxSeg>), grid, block, 0, s, t);
   return hipGetLastError();
 }
 
