@@ -703,7 +703,12 @@ hipError_t pick_r(SegTable& t, int rsel, hipStream_t s) {
   int64_t rows = 0;
   for (int i = 0; i < t.count; ++i) rows += t.s[i].N;
   const int64_t slots = rows / (64 / LPR);
-  int r = rsel ? rsel : slots <= 1024 ? 1 : (H2 && KS == 1) ? 4 : 2;
+  // f32 x with K in one wave: four rows when that, and not two, gives every
+  // wave a single row group (16 waves per CU; grouped 2 x 5632 x 2048 Q4K
+  // gate+up 6.27 -> 5.65 us, where smaller launches and the large heads were
+  // slower at four)
+  const bool four_fits = KS == 1 && LPR == 64 && rows / 2 > 256 * 16 && (rows + 3) / 4 <= 256 * 16;
+  int r = rsel ? rsel : slots <= 1024 ? 1 : ((H2 && KS == 1) || four_fits) ? 4 : 2;
   if constexpr (H2 && KS == 1 && UPL == 1) {
     if (r == 8) return go<FMT, XF16, LPR, UPL, 8, KS>(t, s);
   } else {
