@@ -300,3 +300,18 @@ def test_decode_sweep_launch_configuration(qmv, batch):
                                 oracle.tolerance_bound(W32, xv, TAU["matvec"]))
         _say(name, batch, r)
         assert r["ok"], (name, batch, r)
+
+
+@pytest.mark.parametrize("fmt,shapes", [("q4k", [5632, 5632]), ("q6k", [5000, 4000, 100]), ("q8_0", [8300])])
+def test_grouped_f32_four_row_groups(qmv, fmt, shapes):
+    """K = 2048 with f32 activations and 8193..16384 rows in one launch: the
+    launch takes four rows per lane group (every wave then has one row group),
+    where each matrix on its own (at most 8192 rows) takes two.  Sampled rows
+    match the oracle, and the grouped call equals the single calls bit for bit
+    (a row's lanes are folded in the same order for one, two or four rows)."""
+    K = 2048
+    ws, Wps, xd, items, ys = _run_and_check(qmv, fmt, shapes, K, 1, "f32", True, seed=23, rows_cap=512)
+    for i, (Wp, x, N) in enumerate(items):
+        y1 = qmv.matvec(fmt, Wp, x, N, K)
+        torch.cuda.synchronize()
+        assert torch.equal(y1.view(torch.int32), ys[i].view(torch.int32)), (fmt, i, N)
