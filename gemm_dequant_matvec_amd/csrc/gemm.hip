@@ -248,6 +248,127 @@ __global__ __launch_bounds__(kThreads) void gemm_w4g64_kernel(
   }
 }
 
+// M <= 16 tokens: the tile kernel above gives one workgroup per 64 weight rows
+// (88 for N = 5632) and too few bytes in flight for a launch that is really a
+// weight stream.  Here the 4 waves of a workgroup share 16 weight rows and
+// split the k steps between them (wave w takes steps 4i + w, the workgroup's
+// start rotated by its index), so a launch has 4x the workgroups.  The whole
+// 16-token tile (K <= 2048: at most 64 KB) is staged in LDS once, in the
+// layout above with one more index for the step, so the loop is only weight
+// loads, LDS reads and MFMAs, with P iterations of weight loads in flight and
+// no barrier.  At the end the 4 partial tiles meet in LDS and are added in
+// wave order.  Every load is issued unconditionally with clamped indices, and
+// iterations past the last step contribute zeros, so the wait counts stay exact.
+constexpr int kKsplitMaxK = 2048;
+__global__ __launch_bounds__(kThreads) void gemm_w4g64_ksplit_kernel(
+    const uint8_t* __restrict__ Wq, const uint32_t* __restrict__ Wsz, const uint16_t* __restrict__ X,
+    uint16_t* __restrict__ Y, int M, int N, int K, int vec_store) {
+  constexpr int P = 4;  // iterations of weight loads in flight
+  extern __shared__ u32x4 lds[];  // [step][k half][token row][16-byte chunk], then 4 x 64 partial tiles
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int fr = lane & 15, g = lane >> 4;
+  const int n0 = blockIdx.x * 16;
+  const int nk = (K + KS - 1) / KS;   // 128-k steps
+  const int nit = (nk + 3) / 4;       // iterations (4 steps each)
+  const int nrun = (nit + P - 1) / P * P;
+  const int64_t qrow = K / 2, grow = K / 64;
+  const int row = min(n0 + fr, N - 1);
+  const int rot = int(blockIdx.x) % nit;
+  auto step_of = [&](int it) {  // this wave's step in iteration it (>= nk: none)
+    const int r = it < nit ? (it + rot >= nit ? it + rot - nit : it + rot) : it;
+    return 4 * r + wave;
+  };
+  auto xs = [&](int st, int half, int r, int c) -> u32x4& { return lds[((st * 2 + half) * 16 + r) * 8 + c]; };
+
+  auto wload = [&](int it, u32x4& q, uint32_t& sz) {
+    const int st = min(step_of(it), nk - 1);
+    const int ku = min(st * KS + 32 * g, K - 32);  // first k of this lane's unit
+#if QMV_GEMM_NT
+    q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Wq + row * qrow + ku / 2));
+#else
+    q = *reinterpret_cast<const u32x4*>(Wq + row * qrow + ku / 2);
+#endif
+    sz = Wsz[row * grow + ku / 64];
+  };
+  // weights of the first P iterations first (HBM, the longest wait), then the
+  // token tile: thread t loads chunk (t / 16, t % 16) of every step.  Steps
+  // past the last rewrite the last one with the same values (same thread), so
+  // no store sits behind a branch.
+  u32x4 q0, q1, q2, q3;
+  uint32_t z0, z1, z2, z3;
+  wload(0, q0, z0);
+  wload(1, q1, z1);
+  wload(2, q2, z2);
+  wload(3, q3, z3);
+  {
+    constexpr int NS = kKsplitMaxK / KS;
+    const int r = tid >> 4, c16 = tid & 15;
+    const int m = min(r, M - 1);
+    const int gg = c16 >> 2, ss = c16 & 3;  // k = 32 gg + 8 ss of the step
+    u32x4 xr[NS];
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+      xr[st] = *reinterpret_cast<const u32x4*>(X + int64_t(m) * K + min(min(st, nk - 1) * KS + 8 * c16, K - 8));
+#pragma unroll
+    for (int st = 0; st < NS; ++st) xs(min(st, nk - 1), ss >> 1, r, (4 * (ss & 1) + gg) ^ ((r >> 1) & 7)) = xr[st];
+  }
+  lds_barrier();
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  auto one = [&](int it, u32x4& q, uint32_t& sz) {
+    const int st = step_of(it);
+    const bool kin = st < nk && st * KS + 32 * g < K;  // false past the last step and in a trailing half step
+    float sc = f16_bits_to_f32(sz & 0xFFFFu);
+    float cz = -(sc * f16_bits_to_f32(sz >> 16));
+    if (!kin) sc = cz = 0.0f;
+    const int sr = min(st, nk - 1);
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+      const bf16x8 b = __builtin_bit_cast(bf16x8, xs(sr, s2 >> 1, fr, (4 * (s2 & 1) + g) ^ ((fr >> 1) & 7)));
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dequant8(q[s2], sc, cz), b, acc, 0, 0, 0);
+    }
+    wload(it + P, q, sz);
+  };
+  for (int it = 0; it < nrun; it += P) {
+    one(it, q0, z0);
+    one(it + 1, q1, z1);
+    one(it + 2, q2, z2);
+    one(it + 3, q3, z3);
+  }
+
+  // the 4 partial tiles, added in wave order; C fragment: lane holds weight
+  // rows n = 4 * (lane / 16) + e, token m = lane % 16
+  f32x4* red = reinterpret_cast<f32x4*>(lds + nk * 256);
+  red[wave * 64 + lane] = acc;
+  lds_barrier();
+  if (wave == 0) {
+    const f32x4 v = ((red[lane] + red[64 + lane]) + red[128 + lane]) + red[192 + lane];
+    const int n = n0 + 4 * g, m = fr;
+    if (m < M) {
+      uint16_t* dst = Y + int64_t(m) * N + n;
+      if (vec_store && n + 3 < N) {
+        *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < N) dst[e] = static_cast<uint16_t>(pack_bf16x2(v[e], 0.f) & 0xFFFFu);
+      }
+    }
+  }
+}
+
+hipError_t go_ksplit(const uint8_t* W, const Planes& p, const uint16_t* X, uint16_t* Y, int M, int N, int K,
+                     hipStream_t s) {
+  const int nk = (K + KS - 1) / KS;
+  const size_t lds = size_t(nk) * 256 * sizeof(u32x4) + 4 * 64 * sizeof(f32x4);
+  const dim3 grid((N + 15) / 16);
+  const int vec = (N % 4 == 0) && (reinterpret_cast<uintptr_t>(Y) % 8 == 0);
+  hipLaunchKernelGGL(gemm_w4g64_ksplit_kernel, grid, dim3(kThreads), lds, s, W,
+                     reinterpret_cast<const uint32_t*>(W + p.off[1]), X, Y, M, N, K, vec);
+  return hipGetLastError();
+}
+
 template <int FN, int FM, int S>
 hipError_t go(const uint8_t* W, const Planes& p, const uint16_t* X, uint16_t* Y, int M, int N, int K,
               hipStream_t s) {
@@ -281,9 +402,11 @@ hipError_t launch_gemm(int fmt, int64_t N, int64_t K, int64_t M, const uint8_t* 
     case 6: return go<1, 2, 6>(W, p, X, Y, m, n, k, s);
     case 7: return go<1, 1, 8>(W, p, X, Y, m, n, k, s);
     case 8: return go<2, 2, 6>(W, p, X, Y, m, n, k, s);
+    case 9: return go<1, 1, 8>(W, p, X, Y, m, n, k, s);  // M <= 16 without the K split
     default: break;
   }
-  // measured on MI355X (5632 x 2048): M = 16 -> <1,1,8>, M = 128 and 512 -> <1,4,4>
+  // measured on MI355X (5632 x 2048): M = 16 -> K split, M = 128 and 512 -> <1,4,4>
+  if (m <= 16 && k <= kKsplitMaxK) return go_ksplit(W, p, X, Y, m, n, k, s);
   if (m <= 16) return go<1, 1, 8>(W, p, X, Y, m, n, k, s);
   if (m <= 32) return go<1, 2, 6>(W, p, X, Y, m, n, k, s);
   return go<1, 4, 4>(W, p, X, Y, m, n, k, s);

@@ -37,6 +37,7 @@ def run_gemm(qmv, N, K, M, key):
 
 
 @pytest.mark.parametrize("N,K,M", [(40, 64, 1), (200, 640, 17), (130, 128, 33), (96, 256, 129),
+                                   (200, 640, 5), (72, 1984, 16), (1000, 2048, 3), (24, 2176, 16),
                                    (5632, 2048, 1), (5632, 2048, 16), (5632, 2048, 17),
                                    (5632, 2048, 128), (5632, 2048, 512)])
 def test_gemm_parity(qmv, N, K, M):
