@@ -32,6 +32,7 @@
 #include <cstdlib>
 
 #include <climits>
+#include <type_traits>
 
 #include "qmv_internal.h"
 
@@ -426,9 +427,20 @@ __device__ __forceinline__ void mfma_segment(const TB& tb, const MSeg& sg, uint3
 
   uint32_t* lds = stage + wave * SD;
 
-  // first chunk of the first tile in flight before the activations are set up
+  // First weight chunk of the first tile in flight before the activations are
+  // set up.  With 8 fragments per wave (one chunk of 256 k per tile) two
+  // register sets take this workgroup's tiles in turn, each refilled two tiles
+  // ahead as soon as its chunk is in LDS, so the next tile's loads are in
+  // flight while one tile is computed; the second set's first loads go out
+  // after the set-up.  A set is never copied while its loads are in flight
+  // (the copy would wait for them).  With 16 fragments (two chunks per tile),
+  // and for Q6K, a second set does not fit in the registers next to the
+  // operands (the kernels spilled): one set is refilled with the following
+  // chunk.
+  constexpr bool TWO = KF == 8 && FMT != QMV_Q6K;
   int tile = bid;  // < ntiles (a segment has at most as many workgroups as tiles)
-  Stage<FMT> R = stg.load(tile, u0);
+  const int ntl = (ntiles - bid + nblk - 1) / nblk;  // tiles of this workgroup
+  Stage<FMT> SA = stg.load(tile, u0), SB;
 
   // ---- A operands of this wave's K slice, built once (zero past K and for
   // vectors >= nv, so those fragments and parts contribute nothing)
@@ -487,24 +499,14 @@ __device__ __forceinline__ void mfma_segment(const TB& tb, const MSeg& sg, uint3
     if ((f & 7) == 7) __builtin_amdgcn_sched_barrier(0);  // at most 8 fragments' raw activations live
   }
 
-  const int nch = (min(KF, U - u0) + 7) >> 3;  // chunks of this wave (>= 1)
-  int buf = 0;
-  for (;;) {
-    float acc0 = 0.0f, acc1 = 0.0f;  // vectors 2G and 2G + 1 of weight row (lane & 15)
-#pragma unroll
-    for (int c = 0; c < KF / 8; ++c) {
-      if (c >= nch) break;
-      stg.store(R, lds);
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      const Stage<FMT> cur = R;
-      // next chunk: the following one of this tile, else the first of the next tile
-      if (c + 1 < nch) R = stg.load(tile, u0 + 8 * (c + 1));
-      else if (tile + nblk < ntiles) R = stg.load(tile + nblk, u0);
-      stg.compute(cur, lds, A + 8 * c, u0 + 8 * c, acc0, acc1);
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // operand reads done before the next store
-    }
+  if constexpr (TWO) {
+    if (ntl > 1) SB = stg.load(tile + nblk, u0);
+  }
 
-    // ---- the W partial sums of this tile meet in LDS, added in wave order
+  int buf = 0;
+  float acc0, acc1;  // vectors 2G and 2G + 1 of weight row (lane & 15)
+  // the W partial sums of a tile meet in LDS, added in wave order
+  auto finish = [&]() {
     float* rb = red + (buf * MW + wave) * 128;
     rb[2 * lane] = acc0;
     rb[2 * lane + 1] = acc1;
@@ -520,7 +522,44 @@ __device__ __forceinline__ void mfma_segment(const TB& tb, const MSeg& sg, uint3
     }
     buf ^= 1;
     tile += nblk;
-    if (tile >= ntiles) break;
+  };
+  if constexpr (!TWO) {
+    const int nch = (min(KF, U - u0) + 7) >> 3;  // chunks of this wave (1 or 2)
+    for (;;) {
+      acc0 = acc1 = 0.0f;
+#pragma unroll
+      for (int c = 0; c < KF / 8; ++c) {
+        if (c >= nch) break;
+        stg.store(SA, lds);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const Stage<FMT> cur = SA;
+        // next chunk: the following one of this tile, else the first of the next tile
+        if (c + 1 < nch) SA = stg.load(tile, u0 + 8 * (c + 1));
+        else if (tile + nblk < ntiles) SA = stg.load(tile + nblk, u0);
+        stg.compute(cur, lds, A + 8 * c, u0 + 8 * c, acc0, acc1);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // operand reads done before the next store
+      }
+      finish();
+      if (tile >= ntiles) return;
+    }
+  } else {
+    // tile number n of this workgroup from set S, which then takes tile n + 2
+    auto run = [&](Stage<FMT>& S, int n) {
+      acc0 = acc1 = 0.0f;
+      stg.store(S, lds);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const Stage<FMT> cur = S;  // its loads are done: a plain copy
+      if (n + 2 < ntl) S = stg.load(tile + 2 * nblk, u0);
+      stg.compute(cur, lds, A, u0, acc0, acc1);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // operand reads done before the next store
+      finish();
+    };
+    for (int n = 0;; n += 2) {
+      run(SA, n);
+      if (n + 1 >= ntl) return;
+      run(SB, n + 1);
+      if (n + 2 >= ntl) return;
+    }
   }
 }
 
@@ -554,8 +593,16 @@ int blocks_override() {
   return v;
 }
 
-// Workgroups: up to 512 per launch (tuning override above), split over the
-// segments in proportion to their tiles, at least one and at most one per tile.
+// Workgroups: up to 256 per launch, one per CU, or 512 for Q6K (tuning
+// override above), split over the segments in proportion to their tiles, at
+// least one and at most one per tile.  Every wave builds its activation
+// operands once per launch (about 500 vector instructions per wave for Q4K,
+// against about 230 per tile), so fewer workgroups that each take more tiles,
+// with the next tile's weights in flight, do less work in all (measured on
+// MI355X, one 1.1B decode step at batch 8: 128 / 192 / 256 / 384 / 512
+// workgroups: 0.937 / 0.831 / 0.794 / 0.832 / 0.828 ms; the grouped Q4K
+// gate+up 11.0 -> 8.6 us).  Q6K keeps one register set, so its tiles run back
+// to back: the 32000 x 2048 head took 22.1 us at 512 and 25.8 at 256.
 template <int FMT, bool XF16, int KF>
 hipError_t go(MTable& t, hipStream_t s) {
   int64_t tiles[kMaxSeg], total = 0;
@@ -564,7 +611,7 @@ hipError_t go(MTable& t, hipStream_t s) {
     total += tiles[i];
   }
   int64_t budget = blocks_override();
-  if (budget <= 0) budget = 512;
+  if (budget <= 0) budget = FMT == QMV_Q6K ? 512 : 256;
   if (budget > total) budget = total;
   int b = 0;
   for (int i = 0; i < t.count; ++i) {
