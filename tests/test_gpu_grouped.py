@@ -130,6 +130,24 @@ def test_grouped_batched_equals_single_calls_bitwise(qmv, fmt):
         assert torch.equal(single.view(torch.int32), y.view(torch.int32))
 
 
+@pytest.mark.parametrize("fmt", wl.FORMATS)
+@pytest.mark.parametrize("batch", [3, 8])
+def test_grouped_batched_several_tiles_per_workgroup(qmv, fmt, batch):
+    # 1066 tiles of 16 rows at K = 2048 against at most 256 workgroups (512
+    # for Q6K): workgroups take two to five tiles each, ragged per segment,
+    # the 8-block kernels taking them with two staging register sets in turn.
+    # Rows sampled for the oracle; the single calls (another split of the
+    # tiles over workgroups) must return the same bits.
+    K = 2048
+    shapes = [5000, 3001, 17, 9000]
+    _say(fmt, batch, shapes)
+    ws, Wps, xd, items, ys = _run_and_check(qmv, fmt, shapes, K, batch, XDT[fmt], False, seed=12, rows_cap=1500)
+    for (Wp, x, N), y in zip(items, ys):
+        single = qmv.matvec(fmt, Wp, x, N, K)
+        torch.cuda.synchronize()
+        assert torch.equal(single.view(torch.int32), y.view(torch.int32)), (fmt, N)
+
+
 def test_grouped_wide_k_falls_back(qmv):
     # K = 16384 with f32 activations needs more activation registers than the
     # grouped single-vector kernel holds: one launch per item instead
