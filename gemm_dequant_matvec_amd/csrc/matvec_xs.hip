@@ -736,6 +736,17 @@ bool dispatch(SegTable& t, int rsel, hipStream_t s, hipError_t* e) {
     return (v == 16 || v == 32 || v == 64) ? v : 0;
   }();
   int lpr = U >= 64 ? 64 : (U > 16 ? 32 : 16);
+  // 17..32 units on a streaming launch (more 4-row groups than the grid holds
+  // waves, so every wave walks several groups): 16 lanes per row with two
+  // units each and one row per lane group (measured on MI355X, 151936 x 1024
+  // Q4K head: 20.2 -> 18.6 us; the 3072 x 1024 up projection, one group per
+  // wave, was slower: 3.08 -> 3.29 us)
+  int64_t rows = 0;
+  for (int i = 0; i < t.count; ++i) rows += t.s[i].N;
+  if (lpr == 32 && U <= 32 && rows > 4 * 256 * 16) {
+    lpr = 16;
+    if (!rsel) rsel = 1;
+  }
   if (lpr_forced && lpr_forced < lpr && (U + lpr_forced - 1) / lpr_forced <= 2) lpr = lpr_forced;
   const int upl = (U + lpr - 1) / lpr;
   // activation registers per unit: 17 (fp16 pairs) or 34 (f32)

@@ -183,7 +183,11 @@ int qmv_matvec(int fmt, int64_t N, int64_t K, int64_t batch, const void* W,
  * run one launch series per format.  Items outside the grouped kernels' range
  * (K above 6144 at batch >= 2, or an activation slice too wide for registers
  * at batch 1) run one qmv_matvec launch each.  Each item's result equals its
- * qmv_matvec result bit for bit.  Dtypes and alignment as qmv_matvec (x_dtype
+ * qmv_matvec result bit for bit, with one exception: at batch 1 with
+ * 512 < K <= 1024, a launch of more than 16384 rows in all gives each row 16
+ * lanes instead of 32, so an item whose single call falls on the other side
+ * of that size is summed in another order (both within the matvec
+ * tolerance).  Dtypes and alignment as qmv_matvec (x_dtype
  * must suit every item's format); 1 <= count <= 4096.
  * Errors: FORMAT, SHAPE, NULL, ALIGN, DTYPE, UNSUPPORTED, OVERFLOW, DEVICE, LAUNCH
  * (the message names the offending item).

@@ -167,6 +167,34 @@ def test_single_vector_k_ranges(qmv, fmt, kcase):
             assert r["ok"], (fmt, N, K, xd, r)
 
 
+NARROW_K = {"q8_0": [544, 1024], "w4a16_g64": [576, 1024], "q4k": [768, 1024], "q6k": [768, 1024]}
+
+
+@pytest.mark.parametrize("fmt", wl.FORMATS)
+def test_single_vector_streaming_narrow_k(qmv, fmt):
+    # 512 < K <= 1024 on more than 16384 rows: 16 lanes per row with two
+    # blocks of 32 each and one row per lane group (at K = 544 / 576 / 768 the
+    # second block of some lanes lies past K).  Sampled rows against the
+    # oracle; a one-hot x returns the dequantized column bit for bit.
+    N = 16389
+    for K in NARROW_K[fmt]:
+        w = wl.gen_weights(fmt, N, K, (41, K, 0))
+        rows = np.unique(np.concatenate([_sample_rows(N, seed=K), np.arange(N - 40, N)]))
+        W32 = oracle.dequant_rows(fmt, w, rows)
+        Wp = pack_dev(qmv, fmt, w)
+        for xd in XDT[fmt]:
+            _say("narrow K", fmt, N, K, xd)
+            x = wl.gen_x(K, 1, xd, (41, K, 1))
+            r, _, _ = check_matvec(qmv, fmt, w, x, xd, rows=rows)
+            assert r["ok"], (fmt, K, xd, r)
+            for k in (0, 33, K - 1):
+                oh = np.zeros((1, K), np.float64)
+                oh[0, k] = 1.0
+                xb = oh.astype(np.float32) if xd == "f32" else wl.to_f16_bits(oh)
+                y = qmv.matvec(fmt, Wp, dev_x(xb, xd), N, K).cpu().numpy()
+                assert np.array_equal(y[0, rows], W32[:, k]), (fmt, K, xd, k)
+
+
 @pytest.mark.parametrize("fmt", ["w4a16_g64", "q6k"])
 def test_one_hot_through_k_split_bit_exact(qmv, fmt):
     # K = 5632 runs split over three waves: every column still comes back
