@@ -30,6 +30,13 @@ AUX_FIELDS = {
     "q6k": ("s", "d"),
 }
 _DTYPES = {torch.float32: 1, torch.float16: 2, torch.bfloat16: 3}
+# (weights per element, bytes per element) of each logical aux array
+_AUX_SHAPE = {
+    "q8_0": {"scale": (32, 2)},
+    "w4a16_g64": {"scale": (64, 2), "zero": (64, 2)},
+    "q4k": {"sc": (32, 1), "m": (32, 1), "d": (256, 2), "dmin": (256, 2)},
+    "q6k": {"s": (16, 1), "d": (256, 2)},
+}
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -99,6 +106,22 @@ def _stream(stream) -> int:
     return stream.cuda_stream
 
 
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
+def _need(t: torch.Tensor, nbytes: int, what: str) -> None:
+    """The C ABI sees only pointers: a buffer shorter than the call will touch
+    is rejected here, before anything reaches the device."""
+    if _nbytes(t) < nbytes:
+        raise ValueError(f"{what} holds {_nbytes(t)} bytes, the call needs {nbytes}")
+
+
+def _need_dtype(t: torch.Tensor, dtype: torch.dtype, what: str) -> None:
+    if t.dtype != dtype:
+        raise ValueError(f"{what} must be {dtype}, got {t.dtype}")
+
+
 def _ptr(t: torch.Tensor | None) -> int | None:
     if t is None:
         return None
@@ -131,6 +154,13 @@ def pack(fmt, logical: dict, N: int | None = None, K: int | None = None, batch: 
     nbytes = packed_bytes(name, N, K, batch)
     if out is None:
         out = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    _need(out, nbytes, "out")
+    _need(q, batch * N * K, "q")
+    for field in AUX_FIELDS[name]:
+        if field not in logical:
+            raise ValueError(f"{name} needs the logical array {field!r}")
+        per = _AUX_SHAPE[name][field]
+        _need(logical[field], batch * N * (K // per[0]) * per[1], field)
     src = QmvLogical()
     src.q = _ptr(q)
     for i, field in enumerate(AUX_FIELDS[name]):
@@ -150,6 +180,8 @@ def matvec(fmt, W: torch.Tensor, x: torch.Tensor, N: int, K: int, y: torch.Tenso
         y = torch.empty((b, N), dtype=torch.float32, device=x.device)
     if x2.dtype not in _DTYPES or y.dtype not in _DTYPES:
         raise ValueError("x / y dtype must be float32, float16 or bfloat16")
+    _need(W, packed_bytes(fmt, N, K), "W")
+    _need(y, b * N * 4, "y")
     _check(_lib.qmv_matvec(_fmt(fmt), N, K, b, _ptr(W), _ptr(x2), _DTYPES[x2.dtype], _ptr(y),
                            _DTYPES[y.dtype], _stream(stream)))
     return y
@@ -164,9 +196,9 @@ def matvec_grouped(fmt, items, K: int, stream=None) -> list:
     Returns the list of y.
     """
     arr = (QmvMatvecItem * len(items))()
-    outs = []
+    outs, rows = [], []
     b = xdt = None
-    for i, it in enumerate(items):
+    for i, it in enumerate(items):  # every size check before any pointer is taken
         W, x, N = it[0], it[1], it[2]
         x2 = x if x.dim() == 2 else x.reshape(1, -1)
         if b is None:
@@ -175,9 +207,16 @@ def matvec_grouped(fmt, items, K: int, stream=None) -> list:
             raise ValueError("all items need x of shape [b][K] and one dtype")
         y = it[3] if len(it) > 3 and it[3] is not None else torch.empty((b, N), dtype=torch.float32,
                                                                           device=x.device)
-        arr[i].N, arr[i].W, arr[i].x, arr[i].y = N, _ptr(W), _ptr(x2), _ptr(y)
-        arr[i].fmt = _fmt(it[4]) if len(it) > 4 and it[4] is not None else 0
+        ifmt = it[4] if len(it) > 4 and it[4] is not None else fmt
+        if ifmt is None:
+            raise ValueError(f"item {i} names no format and the call's fmt is None")
+        _need(W, packed_bytes(ifmt, N, K), f"items[{i}].W")
+        _need(y, b * N * 4, f"items[{i}].y")
+        rows.append((W, x2, N, y, it[4] if len(it) > 4 else None))
         outs.append(y)
+    for i, (W, x2, N, y, ifmt) in enumerate(rows):
+        arr[i].N, arr[i].W, arr[i].x, arr[i].y = N, _ptr(W), _ptr(x2), _ptr(y)
+        arr[i].fmt = _fmt(ifmt) if ifmt is not None else 0
     _check(_lib.qmv_matvec_grouped(0 if fmt is None else _fmt(fmt), K, b, len(items), arr, _DTYPES[xdt],
                                    _DTYPES[torch.float32], _stream(stream)))
     return outs
@@ -193,6 +232,8 @@ def gemm(fmt, W: torch.Tensor, X: torch.Tensor, N: int, K: int, Y: torch.Tensor 
         Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
     if X.dtype not in _DTYPES or Y.dtype not in _DTYPES:
         raise ValueError("X / Y dtype must be float32, float16 or bfloat16")
+    _need(W, packed_bytes(fmt, N, K), "W")
+    _need(Y, M * N * Y.element_size(), "Y")
     _check(_lib.qmv_gemm(_fmt(fmt), N, K, M, _ptr(W), _ptr(X), _DTYPES[X.dtype], _ptr(Y),
                          _DTYPES[Y.dtype], _stream(stream)))
     return Y
@@ -203,6 +244,9 @@ def dequant(fmt, W: torch.Tensor, N: int, K: int, out: torch.Tensor | None = Non
     """Dense f32 [N][K] copy of a packed matrix (bit-exact; inspection/testing)."""
     if out is None:
         out = torch.empty((N, K), dtype=torch.float32, device=W.device)
+    _need(W, packed_bytes(fmt, N, K), "W")
+    _need_dtype(out, torch.float32, "out")
+    _need(out, N * K * 4, "out")
     _check(_lib.qmv_dequant(_fmt(fmt), N, K, _ptr(W), _ptr(out), _stream(stream)))
     return out
 

@@ -28,7 +28,6 @@
 //     K loop is unrolled in chunks so that no load is pending across a loop
 //     back-edge (the compiler drains every load at such an edge).
 // The epilogue rounds to bf16 and writes 4 consecutive outputs (8 bytes) per lane.
-#include <cstdlib>
 #include <utility>
 
 #include "qmv_internal.h"
@@ -389,8 +388,7 @@ hipError_t launch_gemm(int fmt, int64_t N, int64_t K, int64_t M, const uint8_t* 
   const int n = int(N), k = int(K), m = int(M);
   // A/B tuning only: QMV_GEMM_TILE forces one of the tile configurations below.
   static const int forced = [] {
-    const char* e = getenv("QMV_GEMM_TILE");
-    return e ? atoi(e) : -1;
+    return ab_switch("QMV_GEMM_TILE", -1);
   }();
   switch (forced) {
     case 0: return go<1, 8, 4>(W, p, X, Y, m, n, k, s);

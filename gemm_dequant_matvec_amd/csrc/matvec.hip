@@ -24,7 +24,6 @@
 // R rows x B vectors are then reduced across the LPR lanes of the row with a
 // butterfly that halves the value count at every step, so the reduction costs
 // about R*B + log2(LPR) cross-lane exchanges instead of R*B*log2(LPR).
-#include <cstdlib>
 
 #include "qmv_internal.h"
 
@@ -337,8 +336,7 @@ namespace {
 // =2 also sends batch 1 to the matrix-core kernel.
 int mfma_mode() {
   static const int v = [] {
-    const char* e = getenv("QMV_MATVEC_MFMA");
-    return e ? atoi(e) : 1;
+    return ab_switch("QMV_MATVEC_MFMA", 1);
   }();
   return v;
 }

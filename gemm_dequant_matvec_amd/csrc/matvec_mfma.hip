@@ -29,7 +29,6 @@
 // of one MFMA that A and B share leaves the product unchanged; the loaders
 // below pick the one that makes each lane's weight bytes contiguous.
 #include <algorithm>
-#include <cstdlib>
 
 #include <climits>
 #include <type_traits>
@@ -587,8 +586,7 @@ __global__ __launch_bounds__(64 * kMaxWaves<KF>) void matvec_mfma_kernel(const M
 
 int blocks_override() {
   static const int v = [] {
-    const char* e = getenv("QMV_MFMA_BLOCKS");  // A/B tuning only: workgroups per launch
-    return e ? atoi(e) : 0;
+    return ab_switch("QMV_MFMA_BLOCKS", 0);  // A/B tuning only: workgroups per launch
   }();
   return v;
 }

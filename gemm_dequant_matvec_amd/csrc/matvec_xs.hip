@@ -15,7 +15,6 @@
 //    inside 16-lane rows and ds_bpermute only across rows.
 #include <algorithm>
 #include <climits>
-#include <cstdlib>
 #include <type_traits>
 
 #include "qmv_internal.h"
@@ -624,8 +623,7 @@ __global__ __launch_bounds__(KS == 1 ? kThreads : 64 * KS) void matvec_xs_mix_ke
 
 bool double_buffer_forced() {
   static const bool v = [] {
-    const char* e = getenv("QMV_MATVEC_DB");  // A/B tuning only: 1 keeps both register sets always
-    return e && atoi(e) == 1;
+    return ab_switch("QMV_MATVEC_DB", 0) == 1;  // A/B tuning only: 1 keeps both register sets always
   }();
   return v;
 }
@@ -647,8 +645,7 @@ hipError_t go(SegTable& t, hipStream_t s) {
   // with more waves).
   constexpr bool H2 = (FMT == QMV_W4A16_G64 && XF16);
   static const int waves_forced = [] {  // A/B tuning only: waves per CU the grid may fill
-    const char* e = getenv("QMV_MATVEC_WAVES_CU");
-    const int v = e ? atoi(e) : 0;
+    const int v = ab_switch("QMV_MATVEC_WAVES_CU", 0);
     return (v >= 4 && v <= 32) ? v : 0;
   }();
   const int64_t max_blocks =
@@ -720,8 +717,7 @@ hipError_t pick_r(SegTable& t, int rsel, hipStream_t s) {
 
 bool ksplit_off() {
   static const bool v = [] {
-    const char* e = getenv("QMV_MATVEC_KSPLIT");  // A/B tuning only: 0 keeps K in one wave
-    return e && atoi(e) == 0;
+    return ab_switch("QMV_MATVEC_KSPLIT", 1) == 0;  // A/B tuning only: 0 keeps K in one wave
   }();
   return v;
 }
@@ -731,8 +727,7 @@ bool dispatch(SegTable& t, int rsel, hipStream_t s, hipError_t* e) {
   constexpr bool H2 = (FMT == QMV_W4A16_G64 && XF16);
   const int U = t.K / 32;
   static const int lpr_forced = [] {  // A/B tuning only: lanes per row (16, 32 or 64)
-    const char* e = getenv("QMV_MATVEC_LPR");
-    const int v = e ? atoi(e) : 0;
+    const int v = ab_switch("QMV_MATVEC_LPR", 0);
     return (v == 16 || v == 32 || v == 64) ? v : 0;
   }();
   int lpr = U >= 64 ? 64 : (U > 16 ? 32 : 16);
@@ -782,8 +777,7 @@ bool dispatch(SegTable& t, int rsel, hipStream_t s, hipError_t* e) {
 
 int rows_override() {
   static const int v = [] {
-    const char* e = getenv("QMV_MATVEC_ROWS");  // A/B tuning only: rows per lane group (1, 2, 4 or 8)
-    const int r = e ? atoi(e) : 0;
+    const int r = ab_switch("QMV_MATVEC_ROWS", 0);  // A/B tuning only: rows per lane group (1, 2, 4 or 8)
     return (r == 1 || r == 2 || r == 4 || r == 8) ? r : 0;
   }();
   return v;

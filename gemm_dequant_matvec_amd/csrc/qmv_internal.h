@@ -72,6 +72,26 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits) {
   return __builtin_bit_cast(float, bits << 16);
 }
 
+// ------------------------------------------------------- A/B tuning switches
+// Kernel-configuration switches read from the environment exist only in
+// measurement builds (-DQMV_AB_SWITCHES=1).  The shipped library is built
+// without them and always takes the measured default, so every configuration
+// it can launch is one the test suite runs.
+#ifndef QMV_AB_SWITCHES
+#define QMV_AB_SWITCHES 0
+#endif
+#if QMV_AB_SWITCHES
+}  // namespace qmv
+#include <cstdlib>
+namespace qmv {
+inline int ab_switch(const char* name, int dflt) {
+  const char* e = getenv(name);
+  return e ? atoi(e) : dflt;
+}
+#else
+inline int ab_switch(const char*, int dflt) { return dflt; }
+#endif
+
 // ----------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; arguments are already validated.
 

@@ -129,17 +129,39 @@ typedef struct qmv_matvec_item {
   int32_t fmt;   /* this matrix's qmv_format, or 0 for the call's fmt */
 } qmv_matvec_item;
 
-/* ABI version (QMV_ABI_VERSION); *layout_version receives QMV_LAYOUT_VERSION if non-NULL. */
+/*
+ * ABI version (QMV_ABI_VERSION); *layout_version receives QMV_LAYOUT_VERSION
+ * if non-NULL.  Host only, never fails.  A caller that links the library as a
+ * C library (aot-llm README, compiler options: a model built as a static or
+ * shared library with a C API and a symbol prefix) checks both numbers
+ * before it hands over buffers packed by another build.
+ */
 int qmv_abi_version(int* layout_version);
 
-/* Static text for a status code. */
+/*
+ * Static text for a status code ("unknown status" for a value outside
+ * qmv_status).  Host only; the string is never freed.  Status codes and the
+ * message below are how unsupported requests are rejected before any work is
+ * queued, naming what is missing (aot-llm README, supported tensor types:
+ * unsupported types are rejected with a message naming the tensor;
+ * pytensor-ml issue 53, PR 6 item F-28: unsupported combinations fail before
+ * the first token).
+ */
 const char* qmv_status_string(int status);
 
-/* Thread-local message of the last failing call on this thread ("" if none). */
+/*
+ * Thread-local message of the last failing call on this thread ("" after a
+ * call that succeeded); it names the argument, item or capability at fault
+ * (same passages as qmv_status_string).  Valid until the next call on the
+ * same thread.
+ */
 const char* qmv_last_error(void);
 
 /*
- * Bytes of `batch` stacked packed matrices of shape N x K.  Host only.
+ * Bytes of `batch` stacked packed matrices of shape N x K.  Host only.  Every
+ * product is checked for overflow before it is formed, and K must be a whole
+ * number of blocks (pytensor-ml issue 53, PR 15 item F-39: checked block and
+ * tail arithmetic for packed tensors).
  * Errors: FORMAT, SHAPE, NULL (out_bytes), OVERFLOW.
  */
 int qmv_packed_bytes(int fmt, int64_t N, int64_t K, int64_t batch, size_t* out_bytes);

@@ -4,7 +4,10 @@ Each test plants one plausible slip into the oracle (by patching it for the
 duration of the test) and checks that a hand-worked block or a layout pin
 now fails.  The mistakes: sub-block index off by one, sc and m swapped,
 d and dmin swapped, the q6 offset dropped, the W4A16 zero's sign flipped,
-the nibble order swapped.
+the nibble order swapped, the two 8-weight halves of a Q6K qh word swapped,
+and four slips in the tolerance bound (an L1 norm, a missing square root, the
+norm taken over the wrong axis, tau applied twice): mutation tests that must
+fail (pytensor-ml issue 53, PR 2 item F-60).
 """
 import json
 import os
@@ -15,7 +18,7 @@ import oracle
 from oracle import dequantize as dq
 from oracle import layout
 
-from test_oracle_pins import _hand_case, golden
+from test_oracle_pins import _hand_case, golden, q6k_qh_first_word, tolerance_pin_holds
 
 
 def _case(cid):
@@ -79,3 +82,62 @@ def test_nibble_order_swapped_is_caught(monkeypatch):
     buf = oracle.pack_ref("w4a16_g64", w)
     want = {c["id"]: c for c in golden()["packed"]}["w4a16_qs_bytes"]["bytes"]
     assert buf[0] != int(want["0"], 16)
+
+
+def test_q6k_qh_halves_swapped_is_caught(monkeypatch):
+    want = int({c["id"]: c for c in golden()["packed"]}["q6k_qh_word"]["word"], 16)
+    assert q6k_qh_first_word() == want
+
+    def swapped(q):
+        N, K = q.shape
+        hi = ((np.asarray(q, dtype=np.uint8) >> 4) & 3).astype(np.uint32).reshape(N, K // 16, 16)
+        w = np.zeros((N, K // 16), dtype=np.uint32)
+        for c in range(4):
+            for f in range(4):
+                k = 8 * (1 - (f >> 1)) + 2 * c + (f & 1)  # the halves exchanged
+                w |= hi[:, :, k] << np.uint32(8 * c + 2 * f)
+        return w
+    monkeypatch.setattr(layout, "_qh_words", swapped)
+    assert q6k_qh_first_word() != want
+
+
+def test_q6k_qh_c_f_roles_swapped_is_caught(monkeypatch):
+    want = int({c["id"]: c for c in golden()["packed"]}["q6k_qh_word"]["word"], 16)
+
+    def swapped(q):
+        N, K = q.shape
+        hi = ((np.asarray(q, dtype=np.uint8) >> 4) & 3).astype(np.uint32).reshape(N, K // 16, 16)
+        w = np.zeros((N, K // 16), dtype=np.uint32)
+        for c in range(4):
+            for f in range(4):
+                k = 8 * (f >> 1) + 2 * c + (f & 1)
+                w |= hi[:, :, k] << np.uint32(8 * f + 2 * c)  # byte and field index exchanged
+        return w
+    monkeypatch.setattr(layout, "_qh_words", swapped)
+    assert q6k_qh_first_word() != want
+
+
+def _bound_with(wnorm, xnorm, tau_pow=1):
+    def fn(W, x, tau):
+        x64 = np.atleast_2d(np.asarray(x, dtype=np.float64))
+        W64 = np.asarray(W, dtype=np.float64)
+        return (tau ** tau_pow) * xnorm(x64)[:, None] * wnorm(W64)[None, :]
+    return fn
+
+
+_L2_rows = lambda a: np.sqrt(np.sum(a * a, axis=1))  # noqa: E731
+
+
+def test_tolerance_mutations_are_caught():
+    assert tolerance_pin_holds(_bound_with(_L2_rows, _L2_rows))          # the definition itself
+    assert tolerance_pin_holds(oracle.tolerance_bound)
+    mutants = {
+        "L1 norm": _bound_with(lambda a: np.sum(np.abs(a), axis=1), lambda a: np.sum(np.abs(a), axis=1)),
+        "no sqrt": _bound_with(lambda a: np.sum(a * a, axis=1), lambda a: np.sum(a * a, axis=1)),
+        "W norm over the wrong axis": _bound_with(lambda a: np.sqrt(np.sum(a * a, axis=0)), _L2_rows),
+        "x norm over the wrong axis": _bound_with(_L2_rows, lambda a: np.sqrt(np.sum(a * a, axis=0))),
+        "tau squared": _bound_with(_L2_rows, _L2_rows, tau_pow=2),
+        "max norm": _bound_with(lambda a: np.max(np.abs(a), axis=1), _L2_rows),
+    }
+    caught = {name: not tolerance_pin_holds(fn) for name, fn in mutants.items()}
+    assert all(caught.values()), caught

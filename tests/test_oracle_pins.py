@@ -264,6 +264,38 @@ def test_tolerance_check_flags_errors():
     assert not r["ok"] and r["max_ratio"] > 1.5
 
 
+def tolerance_pin_holds(bound_fn) -> bool:
+    """The hand-worked tolerance case (tests/golden/hand_blocks.json, "tolerance"):
+    bound_fn(W, x, tau) must give exactly the printed bounds."""
+    c = golden()["tolerance"][0]
+    W = np.array(c["W"], np.float32)
+    x = np.array(c["x"], np.float32)
+    try:
+        got = np.asarray(bound_fn(W, x, c["tau"]), dtype=np.float64)
+    except Exception:
+        return False
+    want = np.array(c["bound"], np.float64)
+    return got.shape == want.shape and bool(np.array_equal(got, want))
+
+
+def test_tolerance_bound_hand_worked():
+    assert tolerance_pin_holds(oracle.tolerance_bound)
+    # a single vector is broadcast as one batch row
+    c = golden()["tolerance"][0]
+    b = oracle.tolerance_bound(np.array(c["W"], np.float32), np.array(c["x"][0], np.float32), 1e-3)
+    assert b.shape == (1, 2) and b[0, 0] == pytest.approx(15e-3) and b[0, 1] == pytest.approx(39e-3)
+
+
+def test_check_within_hand_worked():
+    ref = np.array([[1.0, -2.0]])
+    bound = np.array([[0.5, 0.25]])
+    assert oracle.check_within(np.array([[1.5, -2.25]]), ref, bound)["ok"]        # exactly on the bound
+    assert not oracle.check_within(np.array([[1.5000001, -2.0]]), ref, bound)["ok"]
+    assert not oracle.check_within(np.array([[np.nan, -2.0]]), ref, bound)["ok"]
+    r = oracle.check_within(np.array([[1.25, -2.0]]), ref, bound)
+    assert r["ok"] and r["max_ratio"] == 0.5 and r["max_abs"] == 0.25 and r["n_exact_f32"] == 1
+
+
 # ---------------------------------------------------------------- layout pins
 
 def test_packed_bytes_hand_worked():
@@ -285,12 +317,21 @@ def test_packed_bytes_hand_worked():
     off, nb = layout.plane_offsets("q4k", 1, 256)["meta"]
     assert buf[off:off + nb].tobytes().hex() == G["q4k_meta_record"]["hex"]
 
+    assert q6k_qh_first_word() == int(G["q6k_qh_word"]["word"], 16)
+
+
+Q6K_QH_PATTERN = (0, 1, 2, 3, 3, 2, 1, 0, 1, 3, 0, 2, 2, 0, 3, 1)  # high bits h(k), k = 0..15
+
+
+def q6k_qh_first_word() -> int:
+    """First qh word the oracle packs for q = 16 h(k) + (k mod 16), the golden pattern."""
     k = np.arange(256)
-    w = {"q": (16 * (k % 4)).astype(np.uint8)[None], "s": np.zeros((1, 16), np.int8),
+    h = np.array(Q6K_QH_PATTERN * 16)
+    w = {"q": (16 * h + (k % 16)).astype(np.uint8)[None], "s": np.zeros((1, 16), np.int8),
          "d": np.array([[0]], np.uint16)}
     buf = oracle.pack_ref("q6k", w)
     off, _ = layout.plane_offsets("q6k", 1, 256)["qh"]
-    assert buf[off:off + 4].view(np.uint32)[0] == int(G["q6k_qh_word"]["word"], 16)
+    return int(buf[off:off + 4].view(np.uint32)[0])
 
 
 @pytest.mark.parametrize("fmt", wl.FORMATS)
