@@ -21,13 +21,20 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqmv.so")
 
-FORMATS = {"q8_0": 1, "w4a16_g64": 2, "q4k": 3, "q6k": 4}
-BLOCK = {"q8_0": 32, "w4a16_g64": 64, "q4k": 256, "q6k": 256}
+FORMATS = {"q8_0": 1, "w4a16_g64": 2, "q4k": 3, "q6k": 4, "q4_0": 5, "q5_0": 6, "q5k": 7, "bf16": 8,
+           "i8row": 9}
+BLOCK = {"q8_0": 32, "w4a16_g64": 64, "q4k": 256, "q6k": 256, "q4_0": 32, "q5_0": 32, "q5k": 256, "bf16": 32,
+         "i8row": 32}
 AUX_FIELDS = {
     "q8_0": ("scale",),
     "w4a16_g64": ("scale", "zero"),
     "q4k": ("sc", "m", "d", "dmin"),
     "q6k": ("s", "d"),
+    "q4_0": ("d",),
+    "q5_0": ("d",),
+    "q5k": ("sc", "m", "d", "dmin"),
+    "bf16": (),
+    "i8row": ("scale",),
 }
 _DTYPES = {torch.float32: 1, torch.float16: 2, torch.bfloat16: 3}
 # (weights per element, bytes per element) of each logical aux array
@@ -36,6 +43,10 @@ _AUX_SHAPE = {
     "w4a16_g64": {"scale": (64, 2), "zero": (64, 2)},
     "q4k": {"sc": (32, 1), "m": (32, 1), "d": (256, 2), "dmin": (256, 2)},
     "q6k": {"s": (16, 1), "d": (256, 2)},
+    "q4_0": {"d": (32, 2)},
+    "q5_0": {"d": (32, 2)},
+    "q5k": {"sc": (32, 1), "m": (32, 1), "d": (256, 2), "dmin": (256, 2)},
+    "i8row": {"scale": (None, 4)},  # one per row
 }
 
 if not os.path.exists(LIB_PATH):
@@ -155,12 +166,12 @@ def pack(fmt, logical: dict, N: int | None = None, K: int | None = None, batch: 
     if out is None:
         out = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     _need(out, nbytes, "out")
-    _need(q, batch * N * K, "q")
+    _need(q, batch * N * K * (2 if name == "bf16" else 1), "q")
     for field in AUX_FIELDS[name]:
         if field not in logical:
             raise ValueError(f"{name} needs the logical array {field!r}")
         per = _AUX_SHAPE[name][field]
-        _need(logical[field], batch * N * (K // per[0]) * per[1], field)
+        _need(logical[field], batch * N * (K // per[0] if per[0] else 1) * per[1], field)
     src = QmvLogical()
     src.q = _ptr(q)
     for i, field in enumerate(AUX_FIELDS[name]):

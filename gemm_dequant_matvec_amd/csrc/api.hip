@@ -36,6 +36,11 @@ const char* fmt_name(int fmt) {
     case QMV_W4A16_G64: return "W4A16_G64";
     case QMV_Q4K: return "Q4K";
     case QMV_Q6K: return "Q6K";
+    case QMV_Q4_0: return "Q4_0";
+    case QMV_Q5_0: return "Q5_0";
+    case QMV_Q5K: return "Q5K";
+    case QMV_DENSE_BF16: return "DENSE_BF16";
+    case QMV_I8_ROW: return "I8_ROW";
     default: return "?";
   }
 }
@@ -139,15 +144,19 @@ int qmv_pack(int fmt, int64_t N, int64_t K, int64_t batch, const qmv_logical* sr
   if (!src) return fail(QMV_ERR_NULL, "src is NULL");
   if (!dst) return fail(QMV_ERR_NULL, "dst is NULL");
   if (!src->q) return fail(QMV_ERR_NULL, "src->q is NULL");
-  const int naux = fmt == QMV_Q8_0 ? 1 : fmt == QMV_W4A16_G64 ? 2 : fmt == QMV_Q4K ? 4 : 2;
+  const int naux = qmv::aux_count(fmt);
   for (int i = 0; i < naux; ++i)
     if (!src->aux[i]) return fail(QMV_ERR_NULL, "src->aux[%d] is NULL (%s needs %d)", i, fmt_name(fmt), naux);
   if (!aligned(dst, 16)) return fail(QMV_ERR_ALIGN, "dst is not 16-byte aligned");
+  // f16 arrays (and the bf16 weights) 2-byte aligned, I8_ROW's f32 scales 4-byte
+  const uintptr_t aux_align = fmt == QMV_I8_ROW ? 4 : 2;
   for (int i = 0; i < naux; ++i)
-    if (!aligned(src->aux[i], 2)) return fail(QMV_ERR_ALIGN, "src->aux[%d] is not 2-byte aligned", i);
+    if (!aligned(src->aux[i], aux_align))
+      return fail(QMV_ERR_ALIGN, "src->aux[%d] is not %d-byte aligned", i, int(aux_align));
+  if (fmt == QMV_DENSE_BF16 && !aligned(src->q, 2)) return fail(QMV_ERR_ALIGN, "src->q is not 2-byte aligned");
   const qmv::Planes p = qmv::planes_of(fmt, N, K);
   if (batch > INT64_MAX / p.total) return fail(QMV_ERR_OVERFLOW, "batch * packed bytes overflows");
-  if ((N * K + 255) / 256 >= (int64_t(1) << 31))
+  if ((N * K * (fmt == QMV_DENSE_BF16 ? 2 : 1) + 255) / 256 >= (int64_t(1) << 31))
     return fail(QMV_ERR_OVERFLOW, "matrix too large for one pack launch");
   if ((st = check_device())) return st;
   return launched(qmv::launch_pack(fmt, N, K, batch, *src, static_cast<uint8_t*>(dst), as_stream(stream)),

@@ -51,6 +51,41 @@ __global__ void dequant_units(const uint8_t* __restrict__ W, int64_t off1, int64
       w[2 * i] = ds * static_cast<float>(qs[i] & 15u) - dm;
       w[2 * i + 1] = ds * static_cast<float>(qs[i] >> 4) - dm;
     }
+  } else if constexpr (FMT == QMV_Q4_0 || FMT == QMV_Q5_0 || FMT == QMV_Q5K) {
+    const uint8_t* qs = W + n * (K / 2) + 16 * u;
+    uint32_t qh = 0;
+    if constexpr (FMT != QMV_Q4_0) qh = reinterpret_cast<const uint32_t*>(W + off1)[n * (K / 32) + u];
+    float ds, dm, off;
+    if constexpr (FMT == QMV_Q5K) {
+      const uint32_t* rec = reinterpret_cast<const uint32_t*>(W + off2) + 4 * (n * (K / 256) + u / 8);
+      const float d = f16_bits_to_f32(rec[0] & 0xFFFFu), dmin = f16_bits_to_f32(rec[0] >> 16);
+      const uint64_t lo = uint64_t(rec[1]) | (uint64_t(rec[2]) << 32);
+      const uint64_t hi = uint64_t(rec[2] >> 16) | (uint64_t(rec[3]) << 16);
+      const int j = static_cast<int>(u & 7);
+      ds = d * static_cast<float>((lo >> (6 * j)) & 63u);
+      dm = dmin * static_cast<float>((hi >> (6 * j)) & 63u);
+      off = 0.0f;
+    } else {
+      const int64_t dpl = FMT == QMV_Q4_0 ? off1 : off2;
+      ds = f16_bits_to_f32(reinterpret_cast<const uint16_t*>(W + dpl)[n * (K / 32) + u]);
+      dm = 0.0f;
+      off = FMT == QMV_Q4_0 ? 8.0f : 16.0f;
+    }
+    for (int k = 0; k < 32; ++k) {
+      // fifth bit of weight k = 8i + 2c + e sits at bit 8c + 2i + e of qh
+      const int i = k >> 3, c = (k & 7) >> 1, e = k & 1;
+      const uint32_t lo4 = (k & 1) ? (qs[k >> 1] >> 4) : (qs[k >> 1] & 15u);
+      const uint32_t q = lo4 | (((qh >> (8 * c + 2 * i + e)) & 1u) << 4);
+      if constexpr (FMT == QMV_Q5K) w[k] = ds * static_cast<float>(q) - dm;
+      else w[k] = ds * (static_cast<float>(q) - off);
+    }
+  } else if constexpr (FMT == QMV_DENSE_BF16) {
+    const uint16_t* b = reinterpret_cast<const uint16_t*>(W) + n * K + 32 * u;
+    for (int k = 0; k < 32; ++k) w[k] = bf16_bits_to_f32(b[k]);
+  } else if constexpr (FMT == QMV_I8_ROW) {
+    const int8_t* qs = reinterpret_cast<const int8_t*>(W) + n * K + 32 * u;
+    const float sc = reinterpret_cast<const float*>(W + off1)[n];
+    for (int k = 0; k < 32; ++k) w[k] = sc * static_cast<float>(qs[k]);
   } else {  // QMV_Q6K
     const uint8_t* ql = W + n * (K / 2) + 16 * u;
     const uint32_t* qh = reinterpret_cast<const uint32_t*>(W + off1) + n * (K / 16) + 2 * u;
@@ -93,6 +128,26 @@ hipError_t launch_dequant(int fmt, int64_t N, int64_t K, const uint8_t* W, float
       break;
     case QMV_Q6K:
       hipLaunchKernelGGL(dequant_units<QMV_Q6K>, grid, dim3(kThreads), 0, s, W, p.off[1], p.off[2],
+                         p.off[3], N, K, out);
+      break;
+    case QMV_Q4_0:
+      hipLaunchKernelGGL(dequant_units<QMV_Q4_0>, grid, dim3(kThreads), 0, s, W, p.off[1], p.off[2],
+                         p.off[3], N, K, out);
+      break;
+    case QMV_Q5_0:
+      hipLaunchKernelGGL(dequant_units<QMV_Q5_0>, grid, dim3(kThreads), 0, s, W, p.off[1], p.off[2],
+                         p.off[3], N, K, out);
+      break;
+    case QMV_Q5K:
+      hipLaunchKernelGGL(dequant_units<QMV_Q5K>, grid, dim3(kThreads), 0, s, W, p.off[1], p.off[2],
+                         p.off[3], N, K, out);
+      break;
+    case QMV_DENSE_BF16:
+      hipLaunchKernelGGL(dequant_units<QMV_DENSE_BF16>, grid, dim3(kThreads), 0, s, W, p.off[1], p.off[2],
+                         p.off[3], N, K, out);
+      break;
+    case QMV_I8_ROW:
+      hipLaunchKernelGGL(dequant_units<QMV_I8_ROW>, grid, dim3(kThreads), 0, s, W, p.off[1], p.off[2],
                          p.off[3], N, K, out);
       break;
     default:

@@ -102,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void matvec_kernel(
 
 #pragma unroll 2
   for (int u = l; u < U; u += LPR) {
-    if constexpr (FMT == QMV_Q8_0) {
+    if constexpr (FMT == QMV_Q8_0 || FMT == QMV_I8_ROW) {
       uint4 q[R][2];
       float s[R];
 #pragma unroll
@@ -110,7 +110,10 @@ __global__ __launch_bounds__(kThreads) void matvec_kernel(
         const uint4* p = reinterpret_cast<const uint4*>(W + int64_t(row[r]) * K) + 2 * u;
         q[r][0] = p[0];
         q[r][1] = p[1];
-        s[r] = f16_bits_to_f32(reinterpret_cast<const uint16_t*>(W + off1)[int64_t(row[r]) * (K >> 5) + u]);
+        if constexpr (FMT == QMV_Q8_0)
+          s[r] = f16_bits_to_f32(reinterpret_cast<const uint16_t*>(W + off1)[int64_t(row[r]) * (K >> 5) + u]);
+        else
+          s[r] = reinterpret_cast<const float*>(W + off1)[row[r]];
       }
 #pragma unroll
       for (int b = 0; b < B; ++b) {
@@ -133,6 +136,34 @@ __global__ __launch_bounds__(kThreads) void matvec_kernel(
         }
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r][b] = fmaf(s[r], qx[r], acc[r][b]);
+      }
+    } else if constexpr (FMT == QMV_DENSE_BF16) {
+      uint4 q[R][4];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const uint4* p = reinterpret_cast<const uint4*>(W + (int64_t(row[r]) * K + 32 * u) * 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[r][i] = p[i];
+      }
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const int bb = min(b, nb - 1);
+        const float4* xp = reinterpret_cast<const float4*>(static_cast<const float*>(xv) + int64_t(bb) * K) + 8 * u;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float4 xx = xp[i];  // x[4i .. 4i + 3]: weights 4i .. 4i + 3 are words 2 (i % 2), +1 of q[i / 2]
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const uint4 qq = q[r][i >> 1];
+            const uint32_t w0 = (i & 1) ? qq.z : qq.x, w1 = (i & 1) ? qq.w : qq.y;
+            float t = acc[r][b];
+            t = fmaf(__builtin_bit_cast(float, w0 << 16), xx.x, t);
+            t = fmaf(__builtin_bit_cast(float, w0 & 0xFFFF0000u), xx.y, t);
+            t = fmaf(__builtin_bit_cast(float, w1 << 16), xx.z, t);
+            t = fmaf(__builtin_bit_cast(float, w1 & 0xFFFF0000u), xx.w, t);
+            acc[r][b] = t;
+          }
+        }
       }
     } else if constexpr (FMT == QMV_W4A16_G64 && XF16) {
       uint4 q[R];
@@ -190,15 +221,22 @@ __global__ __launch_bounds__(kThreads) void matvec_kernel(
       float sA[R], mA[R];          // per-unit multiplier of sum q x, and of sum x
       float sB[R];                 // Q6K: second sub-block's multiplier
       uint2 qh[R];
+      uint32_t qh5[R];             // Q5_0 / Q5K fifth bits of the unit
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         q[r] = reinterpret_cast<const uint4*>(W + int64_t(row[r]) * (K >> 1))[u];
-        if constexpr (FMT == QMV_W4A16_G64) {
+        if constexpr (FMT == QMV_Q5_0 || FMT == QMV_Q5K)
+          qh5[r] = reinterpret_cast<const uint32_t*>(W + off1)[int64_t(row[r]) * (K >> 5) + u];
+        if constexpr (FMT == QMV_Q4_0 || FMT == QMV_Q5_0) {
+          const int64_t dpl = FMT == QMV_Q4_0 ? off1 : off2;
+          sA[r] = f16_bits_to_f32(reinterpret_cast<const uint16_t*>(W + dpl)[int64_t(row[r]) * (K >> 5) + u]);
+          mA[r] = FMT == QMV_Q4_0 ? 8.0f : 16.0f;
+        } else if constexpr (FMT == QMV_W4A16_G64) {
           const uint32_t sz = reinterpret_cast<const uint32_t*>(W + off1)[int64_t(row[r]) * (K >> 6) + (u >> 1)];
           sA[r] = f16_bits_to_f32(sz & 0xFFFFu);
           mA[r] = f16_bits_to_f32(sz >> 16);
-        } else if constexpr (FMT == QMV_Q4K) {
-          const uint4 rec = reinterpret_cast<const uint4*>(W + off1)[int64_t(row[r]) * (K >> 8) + (u >> 3)];
+        } else if constexpr (FMT == QMV_Q4K || FMT == QMV_Q5K) {
+          const uint4 rec = reinterpret_cast<const uint4*>(W + (FMT == QMV_Q4K ? off1 : off2))[int64_t(row[r]) * (K >> 8) + (u >> 3)];
           const int j = u & 7;
           const uint64_t lo = uint64_t(rec.y) | (uint64_t(rec.z) << 32);
           const uint64_t hi = uint64_t(rec.z >> 16) | (uint64_t(rec.w) << 16);
@@ -249,6 +287,9 @@ __global__ __launch_bounds__(kThreads) void matvec_kernel(
               const int f = (i & 1) * 2;
               ev |= ((h >> (2 * f)) & 0x03030303u) << 4;
               od |= ((h >> (2 * f + 2)) & 0x03030303u) << 4;
+            } else if constexpr (FMT == QMV_Q5_0 || FMT == QMV_Q5K) {
+              ev |= ((qh5[r] >> (2 * i)) & 0x01010101u) << 4;
+              od |= ((qh5[r] >> (2 * i + 1)) & 0x01010101u) << 4;
             }
             float t = qx[r][part];
 #pragma unroll
@@ -261,9 +302,9 @@ __global__ __launch_bounds__(kThreads) void matvec_kernel(
         }
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          if constexpr (FMT == QMV_W4A16_G64) {
+          if constexpr (FMT == QMV_W4A16_G64 || FMT == QMV_Q4_0 || FMT == QMV_Q5_0) {
             acc[r][b] = fmaf(sA[r], fmaf(-mA[r], sx[0], qx[r][0]), acc[r][b]);
-          } else if constexpr (FMT == QMV_Q4K) {
+          } else if constexpr (FMT == QMV_Q4K || FMT == QMV_Q5K) {
             acc[r][b] = fmaf(sA[r], qx[r][0], acc[r][b]);
             acc[r][b] = fmaf(-mA[r], sx[0], acc[r][b]);
           } else {  // Q6K
@@ -370,6 +411,11 @@ hipError_t launch_matvec(int fmt, int64_t N, int64_t K, int64_t batch, const uin
         break;
       case QMV_Q4K: e = pick_lpr<QMV_Q4K, false>(W, p, xb, yb, int(N), int(K), nb, s); break;
       case QMV_Q6K: e = pick_lpr<QMV_Q6K, false>(W, p, xb, yb, int(N), int(K), nb, s); break;
+      case QMV_Q4_0: e = pick_lpr<QMV_Q4_0, false>(W, p, xb, yb, int(N), int(K), nb, s); break;
+      case QMV_Q5_0: e = pick_lpr<QMV_Q5_0, false>(W, p, xb, yb, int(N), int(K), nb, s); break;
+      case QMV_Q5K: e = pick_lpr<QMV_Q5K, false>(W, p, xb, yb, int(N), int(K), nb, s); break;
+      case QMV_DENSE_BF16: e = pick_lpr<QMV_DENSE_BF16, false>(W, p, xb, yb, int(N), int(K), nb, s); break;
+      case QMV_I8_ROW: e = pick_lpr<QMV_I8_ROW, false>(W, p, xb, yb, int(N), int(K), nb, s); break;
       default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;

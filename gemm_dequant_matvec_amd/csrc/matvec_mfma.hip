@@ -655,6 +655,11 @@ bool launch_table(int fmt, MTable& t, int x_dtype, hipStream_t s, hipError_t* er
   }
 }
 
+// Formats this kernel takes (the others run on the general kernel).
+bool has_kernel(int fmt) {
+  return fmt == QMV_Q8_0 || fmt == QMV_W4A16_G64 || fmt == QMV_Q4K || fmt == QMV_Q6K;
+}
+
 bool fits(int fmt, int64_t N, int64_t K) {
   // the kernel addresses planes with 32-bit offsets; K up to 12 waves x 16 blocks
   return planes_of(fmt, N, K).total < (int64_t(1) << 31) && K / 32 <= 12 * 16;
@@ -666,7 +671,7 @@ bool fits(int fmt, int64_t N, int64_t K) {
 // shapes outside this kernel's range (K > 6144, packed matrix >= 2 GiB).
 bool launch_matvec_mfma(int fmt, int64_t N, int64_t K, int nv, const uint8_t* W, const void* x, int x_dtype,
                         float* y, hipStream_t s, hipError_t* err) {
-  if (!fits(fmt, N, K)) return false;
+  if (!has_kernel(fmt) || !fits(fmt, N, K)) return false;
   const Planes p = planes_of(fmt, N, K);
   MTable t{};
   t.count = 1;
@@ -685,8 +690,8 @@ bool launch_matvec_mfma(int fmt, int64_t N, int64_t K, int nv, const uint8_t* W,
 bool launch_matvec_grouped_mfma(int fmt, int64_t K, int64_t batch, int count, const qmv_matvec_item* items,
                                 int x_dtype, hipStream_t s, hipError_t* err) {
   auto eff = [&](int i) { return items[i].fmt ? items[i].fmt : fmt; };
-  for (int i = 0; i < count; ++i)
-    if (!fits(eff(i), items[i].N, K)) return false;
+  for (int i = 0; i < count; ++i)  // decided before anything is launched
+    if (!has_kernel(eff(i)) || !fits(eff(i), items[i].N, K)) return false;
   const int64_t xel = (x_dtype == QMV_F16) ? 2 : 4;
   auto run = [&](int tfmt, const int* idx, int n) {
     for (int64_t b0 = 0; b0 < batch; b0 += 8) {
@@ -721,7 +726,7 @@ bool launch_matvec_grouped_mfma(int fmt, int64_t K, int64_t batch, int count, co
     for (int i = 0; i < count; ++i) idx[i] = i;
     return run(same ? eff(0) : kMixM, idx, count);
   }
-  for (int f = 1; f <= 4; ++f) {
+  for (int f = 1; f <= kNumFormats; ++f) {
     int n = 0;
     for (int i = 0; i < count; ++i)
       if (eff(i) == f) idx[n++] = i;

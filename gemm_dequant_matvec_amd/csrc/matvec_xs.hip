@@ -147,6 +147,16 @@ template <>
 struct Raw<QMV_Q4K> { uint4 q; uint4 meta; };
 template <>
 struct Raw<QMV_Q6K> { uint4 q; uint2 qh; uint32_t s2; uint32_t d; };
+template <>
+struct Raw<QMV_Q4_0> { uint4 q; uint32_t d; };
+template <>
+struct Raw<QMV_Q5_0> { uint4 q; uint32_t qh; uint32_t d; };
+template <>
+struct Raw<QMV_Q5K> { uint4 q; uint32_t qh; uint4 meta; };
+template <>
+struct Raw<QMV_DENSE_BF16> { uint4 q[4]; };
+template <>
+struct Raw<QMV_I8_ROW> { uint4 q0, q1; uint32_t sc; };
 
 // Weight planes are read through raw buffer resources: an offset at or past
 // the plane size returns zeros without touching memory.  Rows past N and row
@@ -199,11 +209,31 @@ __device__ __forceinline__ Raw<FMT> load_raw(const Geo& g, int row, int u, bool 
   } else if constexpr (FMT == QMV_Q4K) {
     r.q = bl128<kNT>(g.q, (R * (K >> 1) + 16u * U) | bad);
     r.meta = bl128<0>(g.p1, ((R * (K >> 8) + (U >> 3)) * 16u) | bad);
-  } else {
+  } else if constexpr (FMT == QMV_Q6K) {
     r.q = bl128<kNT>(g.q, (R * (K >> 1) + 16u * U) | bad);
     r.qh = bl64<kNT>(g.p1, ((R * (K >> 5) + U) * 8u) | bad);
     r.s2 = __builtin_amdgcn_raw_buffer_load_b16(g.p2, int(((R * (K >> 5) + U) * 2u) | bad), 0, 0);
     r.d = __builtin_amdgcn_raw_buffer_load_b16(g.p3, int(((R * (K >> 8) + (U >> 3)) * 2u) | bad), 0, 0);
+  } else if constexpr (FMT == QMV_Q4_0) {
+    r.q = bl128<kNT>(g.q, (R * (K >> 1) + 16u * U) | bad);
+    r.d = __builtin_amdgcn_raw_buffer_load_b16(g.p1, int(((R * (K >> 5) + U) * 2u) | bad), 0, 0);
+  } else if constexpr (FMT == QMV_Q5_0) {
+    r.q = bl128<kNT>(g.q, (R * (K >> 1) + 16u * U) | bad);
+    r.qh = __builtin_amdgcn_raw_buffer_load_b32(g.p1, int(((R * (K >> 5) + U) * 4u) | bad), 0, kNT);
+    r.d = __builtin_amdgcn_raw_buffer_load_b16(g.p2, int(((R * (K >> 5) + U) * 2u) | bad), 0, 0);
+  } else if constexpr (FMT == QMV_Q5K) {
+    r.q = bl128<kNT>(g.q, (R * (K >> 1) + 16u * U) | bad);
+    r.qh = __builtin_amdgcn_raw_buffer_load_b32(g.p1, int(((R * (K >> 5) + U) * 4u) | bad), 0, kNT);
+    r.meta = bl128<0>(g.p2, ((R * (K >> 8) + (U >> 3)) * 16u) | bad);
+  } else if constexpr (FMT == QMV_DENSE_BF16) {
+    const uint32_t o = ((R * K + 32u * U) * 2u) | bad;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.q[i] = bl128<kNT>(g.q, o + 16u * i);
+  } else {  // QMV_I8_ROW
+    const uint32_t o = (R * K + 32u * U) | bad;
+    r.q0 = bl128<kNT>(g.q, o);
+    r.q1 = bl128<kNT>(g.q, o + 16u);
+    r.sc = __builtin_amdgcn_raw_buffer_load_b32(g.p1, int((R * 4u) | bad), 0, 0);
   }
   return r;
 }
@@ -299,7 +329,7 @@ __device__ __forceinline__ float unit_dot(const Raw<FMT>& w, const XUnit<FMT == 
     const float s = f16_bits_to_f32(w.sz & 0xFFFFu);
     const float zo = 1024.0f + f16_bits_to_f32(w.sz >> 16);  // exact
     return fmaf(s, fmaf(-zo, xu.s, dot), acc);
-  } else if constexpr (FMT == QMV_Q8_0) {
+  } else if constexpr (FMT == QMV_Q8_0 || FMT == QMV_I8_ROW) {
     // code u = q + 128 as t = 0.5 + u / 65536 (u in mantissa bits 8..15 of 0.5)
     float tx = 0.0f;
     const uint32_t wd[8] = {w.q0.x, w.q0.y, w.q0.z, w.q0.w, w.q1.x, w.q1.y, w.q1.z, w.q1.w};
@@ -312,7 +342,21 @@ __device__ __forceinline__ float unit_dot(const Raw<FMT>& w, const XUnit<FMT == 
                   xu.v[4 * i + c], tx);
     }
     const float ux = 65536.0f * fmaf(-0.5f, xu.s0, tx);  // sum (q + 128) x
-    return fmaf(f16_bits_to_f32(w.sc), fmaf(-128.0f, xu.s0, ux), acc);
+    const float sc = FMT == QMV_Q8_0 ? f16_bits_to_f32(w.sc) : __builtin_bit_cast(float, w.sc);
+    return fmaf(sc, fmaf(-128.0f, xu.s0, ux), acc);
+  } else if constexpr (FMT == QMV_DENSE_BF16) {
+    // bf16 pairs: the low half widens by a shift, the high half by a mask
+    float t0 = 0.0f, t1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t wd[4] = {w.q[i].x, w.q[i].y, w.q[i].z, w.q[i].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        t0 = fmaf(__builtin_bit_cast(float, wd[c] << 16), xu.v[8 * i + 2 * c], t0);
+        t1 = fmaf(__builtin_bit_cast(float, wd[c] & 0xFFFF0000u), xu.v[8 * i + 2 * c + 1], t1);
+      }
+    }
+    return acc + (t0 + t1);
   } else {
     // 4- and 6-bit codes b as t = 0.5 + b / 256 (b in mantissa bits 16..21 of
     // 0.5, placed by one v_perm_b32): sum b x = 256 (sum t x - sum x / 2)
@@ -327,6 +371,10 @@ __device__ __forceinline__ float unit_dot(const Raw<FMT>& w, const XUnit<FMT == 
         const int f = (i & 1) * 2;
         ev |= ((h >> (2 * f)) & 0x03030303u) << 4;
         od |= ((h >> (2 * f + 2)) & 0x03030303u) << 4;
+      } else if constexpr (FMT == QMV_Q5_0 || FMT == QMV_Q5K) {
+        // fifth bits of word i: bit 8c + 2i (+1 for odd) of qh
+        ev |= ((w.qh >> (2 * i)) & 0x01010101u) << 4;
+        od |= ((w.qh >> (2 * i + 1)) & 0x01010101u) << 4;
       }
       float t = (FMT == QMV_Q6K && i >= 2) ? tb : ta;
 #pragma unroll
@@ -342,7 +390,10 @@ __device__ __forceinline__ float unit_dot(const Raw<FMT>& w, const XUnit<FMT == 
     if constexpr (FMT == QMV_W4A16_G64) {
       const float s = f16_bits_to_f32(w.sz & 0xFFFFu), z = f16_bits_to_f32(w.sz >> 16);
       return fmaf(s, fmaf(-z, xu.s0, qa), acc);
-    } else if constexpr (FMT == QMV_Q4K) {
+    } else if constexpr (FMT == QMV_Q4_0 || FMT == QMV_Q5_0) {
+      constexpr float off = FMT == QMV_Q4_0 ? 8.0f : 16.0f;
+      return fmaf(f16_bits_to_f32(w.d), fmaf(-off, xu.s0, qa), acc);
+    } else if constexpr (FMT == QMV_Q4K || FMT == QMV_Q5K) {
       // sc_j sits at bit 6j and m_j at bit 48 + 6j of the 96-bit field {w, z, y};
       // 32-bit funnel shifts read them from any word pair.  (A 64-bit shift
       // wants an aligned register pair, so the compiler copied the loaded words
@@ -706,6 +757,7 @@ hipError_t pick_r(SegTable& t, int rsel, hipStream_t s) {
   // slower at four)
   const bool four_fits = KS == 1 && LPR == 64 && rows / 2 > 256 * 16 && (rows + 3) / 4 <= 256 * 16;
   int r = rsel ? rsel : slots <= 1024 ? 1 : ((H2 && KS == 1) || four_fits) ? 4 : 2;
+  if constexpr (FMT == QMV_DENSE_BF16) r = r > 2 ? 2 : r;  // 16 weight registers per unit and row
   if constexpr (H2 && KS == 1 && UPL == 1) {
     if (r == 8) return go<FMT, XF16, LPR, UPL, 8, KS>(t, s);
   } else {
@@ -792,6 +844,11 @@ bool launch_table(int fmt, SegTable& t, int x_dtype, hipStream_t s, hipError_t* 
       return f16 ? dispatch<QMV_W4A16_G64, true>(t, rsel, s, err) : dispatch<QMV_W4A16_G64, false>(t, rsel, s, err);
     case QMV_Q4K: return dispatch<QMV_Q4K, false>(t, rsel, s, err);
     case QMV_Q6K: return dispatch<QMV_Q6K, false>(t, rsel, s, err);
+    case QMV_Q4_0: return dispatch<QMV_Q4_0, false>(t, rsel, s, err);
+    case QMV_Q5_0: return dispatch<QMV_Q5_0, false>(t, rsel, s, err);
+    case QMV_Q5K: return dispatch<QMV_Q5K, false>(t, rsel, s, err);
+    case QMV_DENSE_BF16: return dispatch<QMV_DENSE_BF16, false>(t, rsel, s, err);
+    case QMV_I8_ROW: return dispatch<QMV_I8_ROW, false>(t, rsel, s, err);
     case kMix: return dispatch<kMix, false>(t, rsel, s, err);
     default: return false;
   }
@@ -874,7 +931,7 @@ bool launch_matvec_grouped_b1(int fmt, int64_t K, int count, const qmv_matvec_it
     for (int i = 0; i < count; ++i) idx[i] = i;
     return run(same ? eff(0) : kMix, idx, count);
   }
-  for (int f = 1; f <= 4; ++f) {  // one launch series per format present
+  for (int f = 1; f <= kNumFormats; ++f) {  // one launch series per format present
     int n = 0;
     for (int i = 0; i < count; ++i)
       if (eff(i) == f) idx[n++] = i;

@@ -92,6 +92,22 @@ __global__ void pack_q6k_qh(const uint8_t* __restrict__ q, int64_t q_stride,
   dst[blockIdx.y * dst_stride + t] = w;
 }
 
+// Q5_0 / Q5K fifth-bit plane: word t covers 32 weights; bit 8c + 2i + e holds
+// bit 4 of q[32t + 8i + 2c + e], so that after splitting a 32-bit word of the
+// low-nibble plane into its even and odd nibbles (e = 0 / 1), the fifth bits
+// of word i are (qh >> (2i + e)) & 0x01010101, byte for byte.
+__global__ void pack_q5_qh(const uint8_t* __restrict__ q, int64_t q_stride,
+                           uint32_t* __restrict__ dst, int64_t dst_stride, int64_t nwords) {
+  int64_t t = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  if (t >= nwords) return;
+  const uint8_t* q32 = q + blockIdx.y * q_stride + 32 * t;
+  uint32_t w = 0;
+  for (int i = 0; i < 4; ++i)
+    for (int c = 0; c < 4; ++c)
+      for (int e = 0; e < 2; ++e) w |= ((uint32_t(q32[8 * i + 2 * c + e]) >> 4) & 1u) << (8 * c + 2 * i + e);
+  dst[blockIdx.y * dst_stride + t] = w;
+}
+
 }  // namespace
 
 hipError_t launch_pack(int fmt, int64_t N, int64_t K, int64_t batch, const qmv_logical& src,
@@ -144,6 +160,41 @@ hipError_t launch_pack(int fmt, int64_t N, int64_t K, int64_t batch, const qmv_l
                          static_cast<const uint8_t*>(src.aux[1]), nd, dst + p.off[3], p.total, nd);
       break;
     }
+    case QMV_Q4_0:
+    case QMV_Q5_0:
+    case QMV_Q5K: {
+      hipLaunchKernelGGL(pack_nibbles, grid_for(NK / 2, batch), dim3(kThreads), 0, s, q, NK,
+                         dst + p.off[0], p.total, NK / 2);
+      int plane = 1;
+      if (fmt != QMV_Q4_0) {
+        hipLaunchKernelGGL(pack_q5_qh, grid_for(NK / 32, batch), dim3(kThreads), 0, s, q, NK,
+                           reinterpret_cast<uint32_t*>(dst + p.off[1]), p.total / 4, NK / 32);
+        plane = 2;
+      }
+      if (fmt == QMV_Q5K) {
+        const int64_t nsb = N * (K / 256);
+        hipLaunchKernelGGL(pack_q4k_meta, grid_for(nsb, batch), dim3(kThreads), 0, s,
+                           static_cast<const uint8_t*>(src.aux[0]),
+                           static_cast<const uint8_t*>(src.aux[1]),
+                           static_cast<const uint16_t*>(src.aux[2]),
+                           static_cast<const uint16_t*>(src.aux[3]), nsb,
+                           reinterpret_cast<uint4*>(dst + p.off[2]), p.total / 16);
+      } else {
+        const int64_t nd = N * (K / 32) * 2;
+        hipLaunchKernelGGL(copy_bytes, grid_for(nd, batch), dim3(kThreads), 0, s,
+                           static_cast<const uint8_t*>(src.aux[0]), nd, dst + p.off[plane], p.total, nd);
+      }
+      break;
+    }
+    case QMV_DENSE_BF16:
+      hipLaunchKernelGGL(copy_bytes, grid_for(2 * NK, batch), dim3(kThreads), 0, s, q, 2 * NK,
+                         dst + p.off[0], p.total, 2 * NK);
+      break;
+    case QMV_I8_ROW:
+      hipLaunchKernelGGL(copy_bytes, grid_for(NK, batch), dim3(kThreads), 0, s, q, NK, dst + p.off[0], p.total, NK);
+      hipLaunchKernelGGL(copy_bytes, grid_for(4 * N, batch), dim3(kThreads), 0, s,
+                         static_cast<const uint8_t*>(src.aux[0]), 4 * N, dst + p.off[1], p.total, 4 * N);
+      break;
     default:
       return hipErrorInvalidValue;
   }

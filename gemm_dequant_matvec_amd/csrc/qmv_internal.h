@@ -17,12 +17,35 @@ constexpr int kBlockQ8_0 = 32;
 constexpr int kGroupW4 = 64;
 constexpr int kSuper = 256;
 
+constexpr int kNumFormats = 9;  // qmv_format values 1 .. kNumFormats
+
 inline int block_of(int fmt) {
   switch (fmt) {
     case QMV_Q8_0: return kBlockQ8_0;
     case QMV_W4A16_G64: return kGroupW4;
     case QMV_Q4K: return kSuper;
     case QMV_Q6K: return kSuper;
+    case QMV_Q4_0: return 32;
+    case QMV_Q5_0: return 32;
+    case QMV_Q5K: return kSuper;
+    case QMV_DENSE_BF16: return 32;  // the kernels' 32-weight unit
+    case QMV_I8_ROW: return 32;
+    default: return 0;
+  }
+}
+
+// Logical aux arrays qmv_pack reads for each format.
+inline int aux_count(int fmt) {
+  switch (fmt) {
+    case QMV_Q8_0: return 1;
+    case QMV_W4A16_G64: return 2;
+    case QMV_Q4K: return 4;
+    case QMV_Q6K: return 2;
+    case QMV_Q4_0: return 1;
+    case QMV_Q5_0: return 1;
+    case QMV_Q5K: return 4;
+    case QMV_DENSE_BF16: return 0;
+    case QMV_I8_ROW: return 1;
     default: return 0;
   }
 }
@@ -48,6 +71,11 @@ inline Planes planes_of(int fmt, int64_t N, int64_t K) {
     case QMV_Q6K:
       b[0] = N * K / 2; b[1] = N * (K / 16) * 4; b[2] = N * (K / 16); b[3] = N * (K / 256) * 2;
       n = 4; break;
+    case QMV_Q4_0: b[0] = N * K / 2; b[1] = N * (K / 32) * 2; n = 2; break;
+    case QMV_Q5_0: b[0] = N * K / 2; b[1] = N * (K / 32) * 4; b[2] = N * (K / 32) * 2; n = 3; break;
+    case QMV_Q5K: b[0] = N * K / 2; b[1] = N * (K / 32) * 4; b[2] = N * (K / 256) * 16; n = 3; break;
+    case QMV_DENSE_BF16: b[0] = N * K * 2; n = 1; break;
+    case QMV_I8_ROW: b[0] = N * K; b[1] = N * 4; n = 2; break;
     default: break;
   }
   int64_t off = 0;

@@ -22,6 +22,15 @@
  *                  q in 0..15, sc_j and m_j in 0..63
  *   QMV_Q6K        256-weight super-blocks of 16 sub-blocks of 16:
  *                  w = (f32(d) * f32(s_j)) * (f32(q) - 32),  q in 0..63, s_j int8
+ *   QMV_Q4_0       32-weight blocks:  w = f32(d) * (f32(q) - 8),   q in 0..15
+ *   QMV_Q5_0       32-weight blocks:  w = f32(d) * (f32(q) - 16),  q in 0..31
+ *   QMV_Q5K        as QMV_Q4K with q in 0..31
+ *   QMV_DENSE_BF16 w = the bf16 value
+ *   QMV_I8_ROW     one f32 scale per row:  w = scale_n * f32(q),  q int8
+ * The last five are the other weight types the pages' runtimes load: the
+ * q4_0, q5_0 and q5_K tensor types of the aot-llm README (and the llmopt
+ * README's Q5_0 linear parity receipt), the bf16 resident weights of the
+ * zynfer PR's stage M4 and its stage M5 per-row symmetric int8 weights.
  * The scale of weight k is that of block floor(k / block size).  fp16
  * subnormals are honoured.  qmv_dequant reproduces these values bit for bit.
  * qmv_matvec / qmv_gemm may reassociate sums (tolerances below).
@@ -33,8 +42,14 @@
  *   Q4K        q uint8 [N][K];  aux[0] sc uint8 [N][K/32];  aux[1] m uint8 [N][K/32];
  *              aux[2] d f16 [N][K/256];  aux[3] dmin f16 [N][K/256]
  *   Q6K        q uint8 [N][K];  aux[0] s int8 [N][K/16];  aux[1] d f16 [N][K/256]
+ *   Q4_0, Q5_0 q uint8 [N][K];  aux[0] d f16 [N][K/32]
+ *   Q5K        as Q4K
+ *   DENSE_BF16 q bf16 [N][K] (the weights); no aux
+ *   I8_ROW     q int8 [N][K];  aux[0] scale f32 [N]
  * Fields wider than their bit width are masked to it by qmv_pack
- * (4 bits for 4-bit q, 6 bits for Q6K q and for sc / m).
+ * (4 bits for 4-bit q, 5 bits for 5-bit q, 6 bits for Q6K q and for sc / m).
+ * K must be a multiple of the format's block: 32, 64 (W4A16_G64) or 256
+ * (the K-quants); 32 also for DENSE_BF16 and I8_ROW (the kernels' unit).
  *
  * Packed layout, version 1 (QMV_LAYOUT_VERSION).  One matrix is a sequence
  * of planes; every plane starts at a multiple of 256 bytes (plane sizes are
@@ -54,7 +69,18 @@
  *                    q[n][16t + 8*(f>>1) + 2c + (f&1)]
  *              s     N*(K/16) int8
  *              d     N*(K/256) f16
- * Bytes per weight including scales: Q8_0 8.5 bits, W4A16_G64 4.5, Q4K 4.5, Q6K 6.5625.
+ *   Q4_0       qs    as W4A16_G64
+ *              d     N*(K/32) f16:     element n*(K/32) + b = d[n][b]
+ *   Q5_0       qs    as W4A16_G64, low 4 bits of q
+ *              qh    N*(K/32) u32: word (n, u) covers k = 32u..32u+31; its bit
+ *                    8c + 2i + e (c, i in 0..3, e in 0..1) holds bit 4 of
+ *                    q[n][32u + 8i + 2c + e]
+ *              d     as Q4_0
+ *   Q5K        qs, qh as Q5_0;  meta as Q4K
+ *   DENSE_BF16 w     N*K bf16
+ *   I8_ROW     qs    N*K bytes;  scale N f32
+ * Bytes per weight including scales: Q8_0 8.5 bits, W4A16_G64 4.5, Q4K 4.5, Q6K 6.5625,
+ * Q4_0 4.5, Q5_0 5.5, Q5K 5.5, DENSE_BF16 16, I8_ROW 8 + 32/K.
  *
  * Accuracy of the products.  For every output,
  *   |y - y_exact| <= tau * ||W_row||_2 * ||x||_2
@@ -85,14 +111,19 @@
 extern "C" {
 #endif
 
-#define QMV_ABI_VERSION 2
+#define QMV_ABI_VERSION 3
 #define QMV_LAYOUT_VERSION 1
 
 enum qmv_format {
   QMV_Q8_0 = 1,
   QMV_W4A16_G64 = 2,
   QMV_Q4K = 3,
-  QMV_Q6K = 4
+  QMV_Q6K = 4,
+  QMV_Q4_0 = 5,
+  QMV_Q5_0 = 6,
+  QMV_Q5K = 7,
+  QMV_DENSE_BF16 = 8,
+  QMV_I8_ROW = 9
 };
 
 enum qmv_dtype {
@@ -185,7 +216,7 @@ int qmv_pack(int fmt, int64_t N, int64_t K, int64_t batch, const qmv_logical* sr
  * notes: matrix-vector kernels with f32 activations and weights dequantized
  * on the fly; batched prompt notes: each weight decoded once for several
  * activations).  Any batch >= 1 is accepted; up to 8 vectors share one pass
- * over W.
+ * over W.  x_dtype QMV_F16 is taken by QMV_W4A16_G64 only.
  * Errors: FORMAT, SHAPE, NULL, ALIGN, DTYPE, UNSUPPORTED, OVERFLOW, DEVICE, LAUNCH.
  */
 int qmv_matvec(int fmt, int64_t N, int64_t K, int64_t batch, const void* W,

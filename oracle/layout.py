@@ -25,14 +25,29 @@ All multi-byte fields are little-endian.
                          q[n][16t + 8*(f >> 1) + 2c + (f & 1)]
              plane s     N*(K/16) int8  s[n][j]
              plane d     N*(K/256) f16  d[n][t]
+  q4_0       plane qs    as w4a16_g64
+             plane d     N*(K/32) f16   element n*(K/32) + b = d[n][b]
+  q5_0       plane qs    as w4a16_g64 (low 4 bits of q)
+             plane qh    N*(K/32) u32   word (n, u) covers k = 32u..32u+31; its bit
+                         8c + 2i + e (c, i = 0..3, e = 0..1) holds bit 4 of
+                         q[n][32u + 8i + 2c + e]
+             plane d     as q4_0
+  q5k        plane qs    as w4a16_g64 (low 4 bits of q)
+             plane qh    as q5_0
+             plane meta  as q4k
+  bf16       plane w     N*K bf16       element n*K + k = q[n][k]
+  i8row      plane qs    N*K bytes      byte n*K + k = q[n][k] (two's complement)
+             plane scale N f32          element n = scale[n]
 
-Fields are masked to their width (4 bits for nibbles, 6 bits for sc/m/q6).
+Fields are masked to their width (4 bits for nibbles, 5 bits for q5 codes,
+6 bits for sc/m/q6).
 """
 from __future__ import annotations
 
 import numpy as np
 
-BLOCK = {"q8_0": 32, "w4a16_g64": 64, "q4k": 256, "q6k": 256}
+BLOCK = {"q8_0": 32, "w4a16_g64": 64, "q4k": 256, "q6k": 256, "q4_0": 32, "q5_0": 32, "q5k": 256,
+         "bf16": 32, "i8row": 32}
 ALIGN = 256
 
 
@@ -47,6 +62,16 @@ def _planes(fmt: str, N: int, K: int):
     if fmt == "q6k":
         return [("ql", N * K // 2), ("qh", N * (K // 16) * 4), ("s", N * (K // 16)),
                 ("d", N * (K // 256) * 2)]
+    if fmt == "q4_0":
+        return [("qs", N * K // 2), ("d", N * (K // 32) * 2)]
+    if fmt == "q5_0":
+        return [("qs", N * K // 2), ("qh", N * (K // 32) * 4), ("d", N * (K // 32) * 2)]
+    if fmt == "q5k":
+        return [("qs", N * K // 2), ("qh", N * (K // 32) * 4), ("meta", N * (K // 256) * 16)]
+    if fmt == "bf16":
+        return [("w", N * K * 2)]
+    if fmt == "i8row":
+        return [("qs", N * K), ("scale", N * 4)]
     raise ValueError(f"unknown format {fmt!r}")
 
 
@@ -104,6 +129,28 @@ def _qh_unwords(w: np.ndarray, N: int, K: int) -> np.ndarray:
         for f in range(4):
             k = 8 * (f >> 1) + 2 * c + (f & 1)
             hi[:, :, k] = (w >> np.uint32(8 * c + 2 * f)) & 3
+    return hi.reshape(N, K)
+
+
+def _q5_hwords(q: np.ndarray) -> np.ndarray:
+    """The qh plane of q5_0 / q5k: [N][K/32] uint32 from 5-bit q [N][K]."""
+    N, K = q.shape
+    hi = ((np.asarray(q, dtype=np.uint8) >> 4) & 1).astype(np.uint32).reshape(N, K // 32, 32)
+    w = np.zeros((N, K // 32), dtype=np.uint32)
+    for i in range(4):
+        for c in range(4):
+            for e in range(2):
+                w |= hi[:, :, 8 * i + 2 * c + e] << np.uint32(8 * c + 2 * i + e)
+    return w
+
+
+def _q5_unhwords(w: np.ndarray, N: int, K: int) -> np.ndarray:
+    w = w.reshape(N, K // 32).astype(np.uint32)
+    hi = np.zeros((N, K // 32, 32), dtype=np.uint8)
+    for i in range(4):
+        for c in range(4):
+            for e in range(2):
+                hi[:, :, 8 * i + 2 * c + e] = (w >> np.uint32(8 * c + 2 * i + e)) & 1
     return hi.reshape(N, K)
 
 
@@ -167,6 +214,22 @@ def pack_ref(fmt: str, w: dict) -> np.ndarray:
         put("qh", _qh_words(q6))
         put("s", np.asarray(w["s"], dtype=np.int8))
         put("d", _f16_bytes(w["d"]))
+    elif fmt == "q4_0":
+        put("qs", _nibbles(q))
+        put("d", _f16_bytes(w["d"]))
+    elif fmt in ("q5_0", "q5k"):
+        q5 = np.asarray(q, dtype=np.uint8) & 0x1F
+        put("qs", _nibbles(q5 & 0xF))
+        put("qh", _q5_hwords(q5))
+        if fmt == "q5_0":
+            put("d", _f16_bytes(w["d"]))
+        else:
+            put("meta", _q4k_meta(w["sc"], w["m"], w["d"], w["dmin"]))
+    elif fmt == "bf16":
+        put("w", _f16_bytes(q))
+    elif fmt == "i8row":
+        put("qs", np.asarray(q, dtype=np.int8))
+        put("scale", np.asarray(w["scale"], dtype=np.float32))
     else:
         raise ValueError(fmt)
     return out
@@ -197,4 +260,17 @@ def unpack_ref(fmt: str, N: int, K: int, buf) -> dict:
         return {"q": (lo | (hi << 4)).astype(np.uint8),
                 "s": get("s").view(np.int8).reshape(N, K // 16).copy(),
                 "d": get("d").view(np.uint16).reshape(N, K // 256).copy()}
+    if fmt == "q4_0":
+        return {"q": _unnibbles(get("qs"), N, K), "d": get("d").view(np.uint16).reshape(N, K // 32).copy()}
+    if fmt in ("q5_0", "q5k"):
+        q = (_unnibbles(get("qs"), N, K) | (_q5_unhwords(get("qh").view(np.uint32), N, K) << 4)).astype(np.uint8)
+        if fmt == "q5_0":
+            return {"q": q, "d": get("d").view(np.uint16).reshape(N, K // 32).copy()}
+        sc, m, d, dmin = _q4k_unmeta(get("meta").reshape(N, K // 256, 16))
+        return {"q": q, "sc": sc, "m": m, "d": d, "dmin": dmin}
+    if fmt == "bf16":
+        return {"q": get("w").view(np.uint16).reshape(N, K).copy()}
+    if fmt == "i8row":
+        return {"q": get("qs").view(np.int8).reshape(N, K).copy(),
+                "scale": get("scale").view(np.float32).reshape(N).copy()}
     raise ValueError(fmt)

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(q):
 
 
 def test_abi_and_status_strings(q):
-    assert q.abi_version() == (2, 1)
+    assert q.abi_version() == (3, 1)
     for st in range(0, -10, -1):
         assert q._lib.qmv_status_string(st).decode() not in ("", "unknown status")
     assert q._lib.qmv_status_string(-99).decode() == "unknown status"
@@ -56,7 +56,8 @@ def test_packed_bytes_matches_reference_layout(q, fmt, N, mult, batch):
 
 def test_packed_bytes_errors(q):
     out = ctypes.c_size_t(0)
-    assert q.raw_call("qmv_packed_bytes", 9, 4, 32, 1, ctypes.byref(out)) == -2
+    assert q.raw_call("qmv_packed_bytes", 10, 4, 32, 1, ctypes.byref(out)) == -2
+    assert q.raw_call("qmv_packed_bytes", 0, 4, 32, 1, ctypes.byref(out)) == -2
     assert q.raw_call("qmv_packed_bytes", 1, 0, 32, 1, ctypes.byref(out)) == -4
     assert q.raw_call("qmv_packed_bytes", 1, 4, 33, 1, ctypes.byref(out)) == -4
     assert "multiple" in q.last_error()
@@ -139,7 +140,7 @@ def test_grouped_item_format_errors(q):
     items[0].fmt = items[1].fmt = 3
     assert call(0, 256, 1, 3, items, 1, 1, None) == -2
     assert "items[2]" in q.last_error()
-    items[2].fmt = 9
+    items[2].fmt = 10
     assert call(4, 256, 1, 3, items, 1, 1, None) == -2
     items[2].fmt = 2  # W4A16 beside Q4K: f16 activations suit only the W4A16 item
     assert call(0, 256, 1, 3, items, 2, 1, None) == -3

@@ -61,7 +61,8 @@ def _run_and_check(qmv, fmt, shapes, K, batch, x_dtype, shared_x, seed, rows_cap
     return ws, Wps, xd, items, ys
 
 
-XDT = {"q8_0": "f32", "w4a16_g64": "f16", "q4k": "f32", "q6k": "f32"}
+XDT = {"q8_0": "f32", "w4a16_g64": "f16", "q4k": "f32", "q6k": "f32", "q4_0": "f32", "q5_0": "f32", "q5k": "f32",
+       "bf16": "f32", "i8row": "f32"}
 
 
 @pytest.mark.parametrize("fmt", wl.FORMATS)

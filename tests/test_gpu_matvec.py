@@ -13,7 +13,8 @@ from gpu_helpers import check_matvec, dev, dev_x, pack_dev, x_values
 
 pytestmark = pytest.mark.gpu
 
-XDT = {"q8_0": ("f32",), "w4a16_g64": ("f16", "f32"), "q4k": ("f32",), "q6k": ("f32",)}
+XDT = {"q8_0": ("f32",), "w4a16_g64": ("f16", "f32"), "q4k": ("f32",), "q6k": ("f32",), "q4_0": ("f32",),
+       "q5_0": ("f32",), "q5k": ("f32",), "bf16": ("f32",), "i8row": ("f32",)}
 
 
 def _say(*a):
@@ -101,6 +102,11 @@ SHAPES = {  # (N, K) spanning lanes-per-row 16 / 32 / 64, ragged passes and ragg
     "w4a16_g64": [(1, 64), (37, 1024), (300, 2048), (129, 5632)],
     "q4k": [(1, 256), (37, 1024), (300, 3072), (129, 5632)],
     "q6k": [(1, 256), (37, 768), (300, 2048), (129, 5632)],
+    "q4_0": [(1, 32), (37, 576), (300, 2048), (129, 5632)],
+    "q5_0": [(1, 32), (37, 576), (300, 1024), (129, 5632)],
+    "q5k": [(1, 256), (37, 768), (300, 2048), (129, 5632)],
+    "bf16": [(1, 32), (37, 544), (300, 1024), (129, 3072)],
+    "i8row": [(1, 32), (37, 512), (300, 1024), (129, 3072)],
 }
 
 
@@ -124,6 +130,12 @@ MFMA_K = {
     "w4a16_g64": [64, 2048, 2112, 6144, 6208],
     "q4k": [256, 2048, 3328, 6144, 6400],
     "q6k": [256, 2048, 3328, 5632, 6400],
+    # formats the matrix-core kernel does not take: the FMA kernel at 1..64 units
+    "q4_0": [32, 544, 2048, 5632, 6176],
+    "q5_0": [32, 544, 2048, 5632, 6176],
+    "q5k": [256, 768, 2048, 5632, 6400],
+    "bf16": [32, 544, 2048, 3072, 4128],
+    "i8row": [32, 544, 2048, 3072, 4128],
 }
 
 
@@ -149,6 +161,11 @@ B1_K = {
     "w4a16_g64": [2048, 2112, 4096, 5632, 8192, 8256],
     "q4k": [2048, 2304, 4096, 5632, 6144, 6400],
     "q6k": [2048, 2304, 4096, 5632, 6144, 6400],
+    "q4_0": [2048, 2080, 4096, 5632, 6144, 6176],
+    "q5_0": [2048, 2080, 4096, 5632, 6144, 6176],
+    "q5k": [2048, 2304, 4096, 5632, 6144, 6400],
+    "bf16": [2048, 2080, 4096, 5632, 6144, 6176],
+    "i8row": [2048, 2080, 4096, 5632, 6144, 6176],
 }
 
 
@@ -167,7 +184,9 @@ def test_single_vector_k_ranges(qmv, fmt, kcase):
             assert r["ok"], (fmt, N, K, xd, r)
 
 
-NARROW_K = {"q8_0": [544, 1024], "w4a16_g64": [576, 1024], "q4k": [768, 1024], "q6k": [768, 1024]}
+NARROW_K = {"q8_0": [544, 1024], "w4a16_g64": [576, 1024], "q4k": [768, 1024], "q6k": [768, 1024],
+            "q4_0": [544, 1024], "q5_0": [544, 1024], "q5k": [768, 1024], "bf16": [544, 1024],
+            "i8row": [544, 1024]}
 
 
 @pytest.mark.parametrize("fmt", wl.FORMATS)

@@ -6,8 +6,10 @@ now fails.  The mistakes: sub-block index off by one, sc and m swapped,
 d and dmin swapped, the q6 offset dropped, the W4A16 zero's sign flipped,
 the nibble order swapped, the two 8-weight halves of a Q6K qh word swapped,
 and four slips in the tolerance bound (an L1 norm, a missing square root, the
-norm taken over the wrong axis, tau applied twice): mutation tests that must
-fail (pytensor-ml issue 53, PR 2 item F-60).
+norm taken over the wrong axis, tau applied twice), the fifth code bit of
+Q5_0 / Q5K dropped, the Q4_0 / Q5_0 code offsets swapped, and the per-row
+int8 scale applied per column: mutation tests that must fail (pytensor-ml
+issue 53, PR 2 item F-60).
 """
 import json
 import os
@@ -141,3 +143,38 @@ def test_tolerance_mutations_are_caught():
     }
     caught = {name: not tolerance_pin_holds(fn) for name, fn in mutants.items()}
     assert all(caught.values()), caught
+
+
+def test_q5_fifth_bit_dropped_is_caught(monkeypatch):
+    o0, ok = dq.dequant_q5_0, dq.dequant_q5k
+    monkeypatch.setattr(dq, "dequant_q5_0", lambda q, d: o0(np.asarray(q) & 0xF, d))
+    monkeypatch.setattr(dq, "dequant_q5k", lambda q, sc, m, d, dmin: ok(np.asarray(q) & 0xF, sc, m, d, dmin))
+    assert _y(_case("q5_0_e21")) != 1.25
+    assert _y(_case("q5k_e58")) != 25.5
+
+
+def test_q4_0_q5_0_offsets_swapped_is_caught(monkeypatch):
+    # the Q5_0 offset (16) applied to Q4_0 codes and the Q4_0 offset (8) to Q5_0 codes
+    monkeypatch.setattr(dq, "dequant_q4_0", lambda q, d: dq._expand(dq.f16_to_f32(d), 32) * (
+        (np.asarray(q) & 0xF).astype(np.float32) - np.float32(16.0)))
+    monkeypatch.setattr(dq, "dequant_q5_0", lambda q, d: dq._expand(dq.f16_to_f32(d), 32) * (
+        (np.asarray(q) & 0x1F).astype(np.float32) - np.float32(8.0)))
+    assert _y(_case("q4_0_ones")) != -8.0
+    assert _y(_case("q5_0_ones")) != -4.0
+
+
+def test_i8row_scale_per_column_is_caught(monkeypatch):
+    k = np.arange(32)
+    q = np.stack([k - 16, k - 16]).astype(np.int8)
+    scale = np.array([0.75, 2.0], np.float32)
+    x = np.zeros(32, np.float32)
+    x[5] = 1.0
+
+    def pin():
+        return np.array_equal(oracle.matvec_ref(oracle.dequant("i8row", {"q": q, "scale": scale}), x),
+                              [[-8.25, -22.0]])
+    assert pin()
+    monkeypatch.setattr(dq, "dequant_i8row", lambda qq, sc: np.resize(np.asarray(sc, np.float32),
+                                                                        np.shape(qq)[1])[None, :]
+                        * np.asarray(qq, dtype=np.int8).astype(np.float32))
+    assert not pin()

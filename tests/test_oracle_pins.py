@@ -78,10 +78,23 @@ def _hand_case(case):
             w = {"q": (k % 16).astype(np.uint8)[None], "sc": (j + 1).astype(np.uint8)[None],
                  "m": (2 * j).astype(np.uint8)[None], "d": np.array([[0x3800]], np.uint16),
                  "dmin": np.array([[0x3400]], np.uint16)}
-    else:
+    elif fmt == "q6k":
         j = np.arange(16)
         w = {"q": (k % 64).astype(np.uint8)[None], "s": (j - 8).astype(np.int8)[None],
              "d": np.array([[0x3000]], np.uint16)}
+    elif fmt == "q4_0":
+        w = {"q": (k % 16).astype(np.uint8)[None], "d": np.array([[0x3800]], np.uint16)}
+    elif fmt == "q5_0":
+        w = {"q": k.astype(np.uint8)[None], "d": np.array([[0x3400]], np.uint16)}
+    elif fmt == "q5k":
+        j = np.arange(8)
+        w = {"q": (k % 32).astype(np.uint8)[None], "sc": (j + 1).astype(np.uint8)[None],
+             "m": (2 * j).astype(np.uint8)[None], "d": np.array([[0x3800]], np.uint16),
+             "dmin": np.array([[0x3400]], np.uint16)}
+    elif fmt == "bf16":
+        w = {"q": (0x3F80 + k).astype(np.uint16)[None]}
+    else:  # i8row
+        w = {"q": (k - 16).astype(np.int8)[None], "scale": np.array([0.75], np.float32)}
     xs = case["x"]
     if xs == "ones":
         x = np.ones(K, np.float32)
@@ -168,6 +181,51 @@ def test_q6k_unit_d_is_integer_matvec():
 
 # ------------------------------------------------- exactness and closed forms
 
+def test_q4_0_q5_0_unit_scale_are_integer_matvecs():
+    g = np.random.default_rng(12)
+    N, K = 4, 96
+    for fmt, bits, off in (("q4_0", 4, 8), ("q5_0", 5, 16)):
+        q = g.integers(0, 1 << bits, size=(N, K), dtype=np.uint8)
+        w = {"q": q, "d": np.full((N, K // 32), 0x3C00, np.uint16)}
+        x = _rand_int_x(g, 2, K)
+        y = oracle.matvec_ref(oracle.dequant(fmt, w), x)
+        assert np.array_equal(y, (x.astype(np.int64) @ (q.astype(np.int64) - off).T).astype(np.float64))
+
+
+def test_q5k_unit_d_is_integer_matvec():
+    g = np.random.default_rng(13)
+    N, K = 3, 512
+    w = {"q": g.integers(0, 32, size=(N, K), dtype=np.uint8),
+         "sc": g.integers(0, 64, size=(N, K // 32), dtype=np.uint8),
+         "m": g.integers(0, 64, size=(N, K // 32), dtype=np.uint8),
+         "d": np.full((N, K // 256), 0x3C00, np.uint16),
+         "dmin": np.full((N, K // 256), 0x3C00, np.uint16)}
+    x = _rand_int_x(g, 2, K)
+    y = oracle.matvec_ref(oracle.dequant("q5k", w), x)
+    wint = np.repeat(w["sc"].astype(np.int64), 32, axis=1) * w["q"].astype(np.int64) - np.repeat(
+        w["m"].astype(np.int64), 32, axis=1)
+    assert np.array_equal(y, (x.astype(np.int64) @ wint.T).astype(np.float64))
+
+
+def test_i8row_scale_is_per_row_and_bf16_decodes_like_torch():
+    # two rows, scales 0.75 and 2, q = k - 16: x = e5 picks 0.75 * -11 and 2 * -11
+    k = np.arange(32)
+    w = {"q": np.stack([k - 16, k - 16]).astype(np.int8), "scale": np.array([0.75, 2.0], np.float32)}
+    x = np.zeros(32, np.float32)
+    x[5] = 1.0
+    assert np.array_equal(oracle.matvec_ref(oracle.dequant("i8row", w), x), [[-8.25, -22.0]])
+    # unit scale: an integer matvec
+    g = np.random.default_rng(14)
+    q = g.integers(-128, 128, size=(3, 64), dtype=np.int8)
+    xi = _rand_int_x(g, 2, 64)
+    y = oracle.matvec_ref(oracle.dequant("i8row", {"q": q, "scale": np.ones(3, np.float32)}), xi)
+    assert np.array_equal(y, (xi.astype(np.int64) @ q.astype(np.int64).T).astype(np.float64))
+    # bf16 weights are the library conversion's values
+    bits = wl.gen_weights("bf16", 4, 64, (91, 0, 0))["q"]
+    t = torch.from_numpy(bits.astype(np.int16)).view(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(oracle.dequant("bf16", {"q": bits}), t)
+
+
 def test_q4k_single_rounding_matches_f64_difference():
     w = wl.gen_weights("q4k", 64, 1024, (99, 0, 0))
     W = oracle.dequant("q4k", w)
@@ -195,10 +253,21 @@ def test_dequant_exact_rational_on_workload_ranges(fmt):
             elif fmt == "q4k":
                 e = (F(w["d"][n, kk // 256]) * int(w["sc"][n, kk // 32]) * int(w["q"][n, kk])
                      - F(w["dmin"][n, kk // 256]) * int(w["m"][n, kk // 32]))
-            else:
+            elif fmt == "q6k":
                 e = F(w["d"][n, kk // 256]) * int(w["s"][n, kk // 16]) * (int(w["q"][n, kk]) - 32)
-            if fmt == "q4k":
-                assert float(W[n, kk]) == float(np.float32(float(e)))
+            elif fmt == "q4_0":
+                e = F(w["d"][n, kk // 32]) * (int(w["q"][n, kk]) - 8)
+            elif fmt == "q5_0":
+                e = F(w["d"][n, kk // 32]) * (int(w["q"][n, kk]) - 16)
+            elif fmt == "q5k":
+                e = (F(w["d"][n, kk // 256]) * int(w["sc"][n, kk // 32]) * int(w["q"][n, kk])
+                     - F(w["dmin"][n, kk // 256]) * int(w["m"][n, kk // 32]))
+            elif fmt == "bf16":
+                e = Fraction(float(oracle.bf16_to_f64(np.uint16(w["q"][n, kk]))[()]))
+            else:  # i8row: one correctly rounded f32 product
+                e = Fraction(float(w["scale"][n])) * int(w["q"][n, kk])
+            if fmt in ("q4k", "q5k", "i8row"):
+                assert float(W[n, kk]) == float(np.float32(float(e)))  # f64 holds e exactly; one rounding
             else:
                 assert Fraction(float(W[n, kk])) == e
 
@@ -334,6 +403,16 @@ def q6k_qh_first_word() -> int:
     return int(buf[off:off + 4].view(np.uint32)[0])
 
 
+def test_q5_qh_word_hand_worked():
+    G = {c["id"]: c for c in golden()["packed"]}
+    k = np.arange(32)
+    h = np.isin(k, [3, 8, 21, 30]).astype(np.uint8)
+    w = {"q": (16 * h + (k % 16)).astype(np.uint8)[None], "d": np.array([[0x3C00]], np.uint16)}
+    buf = oracle.pack_ref("q5_0", w)
+    off, _ = layout.plane_offsets("q5_0", 1, 32)["qh"]
+    assert buf[off:off + 4].view(np.uint32)[0] == int(G["q5_qh_word"]["word"], 16)
+
+
 @pytest.mark.parametrize("fmt", wl.FORMATS)
 def test_pack_unpack_round_trip(fmt):
     N, K = 7, wl.BLOCK[fmt] * 3
@@ -348,7 +427,8 @@ def test_pack_unpack_round_trip(fmt):
 
 def test_packed_sizes_match_bits_per_weight():
     # plane bytes (without padding) per weight: 8.5, 4.5, 4.5, 6.5625 bits
-    for fmt, bits in (("q8_0", 8.5), ("w4a16_g64", 4.5), ("q4k", 4.5), ("q6k", 6.5625)):
+    for fmt, bits in (("q8_0", 8.5), ("w4a16_g64", 4.5), ("q4k", 4.5), ("q6k", 6.5625), ("q4_0", 4.5),
+                      ("q5_0", 5.5), ("q5k", 5.5), ("bf16", 16.0), ("i8row", 8.0 + 32 / 4096)):
         N, K = 256, 4096
         raw = sum(nb for _, nb in layout._planes(fmt, N, K))
         assert raw * 8 == bits * N * K
@@ -371,6 +451,13 @@ def test_generators_deterministic_and_in_range():
     assert w["sc"].max() <= 63 and w["m"].max() <= 63 and w["q"].max() <= 15
     w = wl.gen_weights("q6k", 64, 512, (92, 0, 3))
     assert w["q"].max() <= 63 and w["s"].min() >= -64 and w["s"].max() <= 63
+    assert wl.gen_weights("q4_0", 64, 512, (92, 0, 4))["q"].max() == 15
+    assert wl.gen_weights("q5_0", 64, 512, (92, 0, 5))["q"].max() == 31
+    w = wl.gen_weights("q5k", 64, 512, (92, 0, 6))
+    assert w["q"].max() == 31 and w["sc"].max() <= 63 and w["m"].max() <= 63
+    w = wl.gen_weights("i8row", 64, 512, (92, 0, 7))
+    assert w["q"].min() >= -127 and w["scale"].dtype == np.float32 and w["scale"].shape == (64,)
+    assert np.all(np.isfinite(oracle.dequant("bf16", wl.gen_weights("bf16", 64, 512, (92, 0, 8)))))
     x1 = wl.gen_x(512, 2, "f32", (92, 0, 0))
     x2 = wl.gen_x(512, 2, "f32", (92, 0, 0))
     assert np.array_equal(x1, x2)

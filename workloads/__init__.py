@@ -13,6 +13,17 @@ Logical (unpacked) arrays, row-major, one entry per weight or per block:
              d, dmin f16 [N][K/256]
   q6k        q uint8 [N][K] in [0, 63]; s int8 [N][K/16] in [-64, 63];
              d f16 [N][K/256]
+  q4_0       q uint8 [N][K] in [0, 15]; d f16 [N][K/32]
+  q5_0       q uint8 [N][K] in [0, 31]; d f16 [N][K/32]
+  q5k        q uint8 [N][K] in [0, 31]; sc, m uint8 [N][K/32] in [0, 63];
+             d, dmin f16 [N][K/256]
+  bf16       q uint16 [N][K]: bf16 bit patterns of the weights themselves
+  i8row      q int8 [N][K] in [-127, 127]; scale f32 [N] (one per row)
+
+The parameter distributions of the last five (formats the pages name but
+give no workload for) follow the nearest given ones: 32-blocks like Q8_0's
+scale, Q5K like Q4K, bf16 weights 0.02 N(0,1), per-row int8 scales like
+Q8_0's but in f32.
 
 f16/bf16 arrays are returned as their uint16 bit patterns.  Scale-like values
 are drawn in float64 and rounded once to fp16 (round to nearest even),
@@ -27,10 +38,12 @@ from __future__ import annotations
 
 import numpy as np
 
-FORMATS = ("q8_0", "w4a16_g64", "q4k", "q6k")
+FORMATS = ("q8_0", "w4a16_g64", "q4k", "q6k", "q4_0", "q5_0", "q5k", "bf16", "i8row")
 
-# Block geometry of each format: (weights per scale block, weights per K-divisibility unit)
-BLOCK = {"q8_0": 32, "w4a16_g64": 64, "q4k": 256, "q6k": 256}
+# K must be a multiple of this for each format (its block, or the kernels'
+# 32-weight unit for the formats without blocks)
+BLOCK = {"q8_0": 32, "w4a16_g64": 64, "q4k": 256, "q6k": 256, "q4_0": 32, "q5_0": 32, "q5k": 256,
+         "bf16": 32, "i8row": 32}
 
 # The field names of each format's logical arrays, in the order the C ABI's
 # qmv_logical.aux[] takes them (q is separate).
@@ -39,6 +52,11 @@ AUX_FIELDS = {
     "w4a16_g64": ("scale", "zero"),
     "q4k": ("sc", "m", "d", "dmin"),
     "q6k": ("s", "d"),
+    "q4_0": ("d",),
+    "q5_0": ("d",),
+    "q5k": ("sc", "m", "d", "dmin"),
+    "bf16": (),
+    "i8row": ("scale",),
 }
 
 
@@ -84,10 +102,24 @@ def gen_weights(fmt: str, N: int, K: int, key: tuple) -> dict:
         out["m"] = g.integers(0, 64, size=(N, K // 32), dtype=np.uint8)
         out["d"] = to_f16_bits(1e-3 * np.abs(g.standard_normal((N, K // 256))))
         out["dmin"] = to_f16_bits(1e-3 * np.abs(g.standard_normal((N, K // 256))))
-    else:  # q6k
+    elif fmt == "q6k":
         out["q"] = g.integers(0, 64, size=(N, K), dtype=np.uint8)
         out["s"] = g.integers(-64, 64, size=(N, K // 16), dtype=np.int8)
         out["d"] = to_f16_bits(1e-3 * np.abs(g.standard_normal((N, K // 256))))
+    elif fmt in ("q4_0", "q5_0"):
+        out["q"] = g.integers(0, 16 if fmt == "q4_0" else 32, size=(N, K), dtype=np.uint8)
+        out["d"] = to_f16_bits(0.01 * np.abs(g.standard_normal((N, K // 32))) + 1e-4)
+    elif fmt == "q5k":
+        out["q"] = g.integers(0, 32, size=(N, K), dtype=np.uint8)
+        out["sc"] = g.integers(0, 64, size=(N, K // 32), dtype=np.uint8)
+        out["m"] = g.integers(0, 64, size=(N, K // 32), dtype=np.uint8)
+        out["d"] = to_f16_bits(1e-3 * np.abs(g.standard_normal((N, K // 256))))
+        out["dmin"] = to_f16_bits(1e-3 * np.abs(g.standard_normal((N, K // 256))))
+    elif fmt == "bf16":
+        out["q"] = to_bf16_bits(0.02 * g.standard_normal((N, K)))
+    else:  # i8row
+        out["q"] = g.integers(-127, 128, size=(N, K), dtype=np.int8)
+        out["scale"] = (0.01 * np.abs(g.standard_normal(N)) + 1e-4).astype(np.float32)
     return out
 
 
@@ -159,6 +191,10 @@ def c5_sweep(batch: int, layers: int = 22):
     return dict(name=f"1.1B decode sweep b{batch}", x_dtype="f32", batch=batch, mats=mats)
 
 
-def bytes_per_weight(fmt: str) -> float:
-    """Algorithmic bytes per weight (quantized fields + scales/mins)."""
-    return {"q8_0": 34 / 32, "w4a16_g64": 36 / 64, "q4k": 144 / 256, "q6k": 210 / 256}[fmt]
+def bytes_per_weight(fmt: str, K: int | None = None) -> float:
+    """Algorithmic bytes per weight (quantized fields + scales/mins); i8row's
+    per-row scale needs the row length K."""
+    if fmt == "i8row":
+        return 1.0 + 4.0 / K
+    return {"q8_0": 34 / 32, "w4a16_g64": 36 / 64, "q4k": 144 / 256, "q6k": 210 / 256,
+            "q4_0": 18 / 32, "q5_0": 22 / 32, "q5k": 176 / 256, "bf16": 2.0}[fmt]
