@@ -22,7 +22,8 @@ What it computes, and where the pages define it:
 Modules:
   fp         exact fp16 / bf16 decoding from the IEEE-754 field definitions
   dequantize per-format dequantization to f32, in the normative order
-  reference  f64 matvec / GEMM and the per-output tolerance bound
+  reference  f64 matvec / GEMM, the per-output tolerance bound, and the fused
+             decode epilogues (bias / residual add, SwiGLU) with their bounds
   layout     reference packer / unpacker of the library's packed layout v1
 
 Parity status: every function here is pinned by `-m "not gpu"` tests against
@@ -31,4 +32,5 @@ hand-worked blocks, library routines and exact rational arithmetic.
 from .fp import f16_to_f32, f16_to_f64, bf16_to_f32, bf16_to_f64  # noqa: F401
 from .dequantize import dequant, dequant_rows  # noqa: F401
 from .reference import matvec_ref, gemm_ref, tolerance_bound, check_within  # noqa: F401
+from .reference import silu_ref, swiglu_ref, swiglu_bound, epilogue_ref, epilogue_bound  # noqa: F401
 from .layout import pack_ref, unpack_ref, packed_bytes_ref  # noqa: F401

@@ -65,3 +65,62 @@ def check_within(y, y_ref, bound) -> dict:
         "n_exact_f32": int(np.sum(y.astype(np.float32) == y_ref.astype(np.float32))),
         "n": int(y.size),
     }
+
+
+# ----------------------------------------------------------------------------
+# Fused decode epilogues (aot-llm README, Metal backend notes: the q/k/v
+# projections take their biases in the epilogue of the matrix kernels, wo and
+# down add the residual in theirs, and gate / up / SwiGLU run as one fused
+# product).  The plain definitions, in f64:
+#
+#   epilogue:  y[b][n] = residual[b][n] + ((W x_b)[n] + bias[n])
+#   SwiGLU:    h[b][n] = silu((W_gate x_b)[n]) * (W_up x_b)[n],
+#              silu(z) = z / (1 + exp(-z))   (the swish with unit slope)
+#
+# Tolerance.  The products carry the matvec bound d = tau ||W_row|| ||x||.
+# The epilogue adds at most two f32 roundings of the result on top:
+#   |y - y*| <= d + 2^-23 (|residual| + |W x + bias|) + 2^-24 |bias|.
+# For SwiGLU, with g*, u* the exact products and dg, du their bounds:
+#   |silu(g) u - silu(g*) u*| <= L dg (|u*| + du) + |silu(g*)| du
+# where L = 1.1 >= max |silu'| = 1.09984 (silu' = s (1 + z (1 - s)), s the
+# logistic function, peaks near z = 2.40), plus the f32 evaluation of silu and the
+# product, allowed 2^-20 |h*| (a few ulp of each step).
+
+SILU_LIP = 1.1
+
+
+def silu_ref(z):
+    z = np.asarray(z, dtype=np.float64)
+    return z / (1.0 + np.exp(-z))
+
+
+def swiglu_ref(g, u):
+    """h = silu(g) * u, elementwise, in f64."""
+    return silu_ref(g) * np.asarray(u, dtype=np.float64)
+
+
+def swiglu_bound(g_ref, u_ref, dg, du):
+    """Bound on |h - h*| from the bounds dg, du of the two products (shapes broadcast)."""
+    g_ref = np.asarray(g_ref, dtype=np.float64)
+    u_ref = np.asarray(u_ref, dtype=np.float64)
+    h = np.abs(swiglu_ref(g_ref, u_ref))
+    return SILU_LIP * dg * (np.abs(u_ref) + du) + np.abs(silu_ref(g_ref)) * du + 2.0 ** -20 * h
+
+
+def epilogue_ref(y_mv, bias=None, residual=None):
+    """residual + (W x + bias) in f64; y_mv is the exact product [b][N]."""
+    y = np.asarray(y_mv, dtype=np.float64)
+    if bias is not None:
+        y = y + np.asarray(bias, dtype=np.float64)[None, :]
+    if residual is not None:
+        y = np.asarray(residual, dtype=np.float64) + y
+    return y
+
+
+def epilogue_bound(bound_mv, y_mv, bias=None, residual=None):
+    """The matvec bound plus the two f32 roundings of the epilogue."""
+    y_mv = np.asarray(y_mv, dtype=np.float64)
+    t = y_mv + (0.0 if bias is None else np.asarray(bias, dtype=np.float64)[None, :])
+    r = 0.0 if residual is None else np.abs(np.asarray(residual, dtype=np.float64))
+    b = 0.0 if bias is None else np.abs(np.asarray(bias, dtype=np.float64))[None, :]
+    return bound_mv + 2.0 ** -23 * (r + np.abs(t)) + 2.0 ** -24 * b
