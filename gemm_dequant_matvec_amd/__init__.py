@@ -76,6 +76,16 @@ _lib.qmv_matvec.argtypes = [_int, _i64, _i64, _i64, _vp, _vp, _int, _vp, _int, _
 _lib.qmv_matvec.restype = _int
 
 
+class QmvEpilogue(ctypes.Structure):
+    _fields_ = [("bias", ctypes.c_void_p), ("residual", ctypes.c_void_p)]
+
+
+_lib.qmv_matvec_ex.argtypes = [_int, _i64, _i64, _i64, _vp, _vp, _int, _vp, _int, ctypes.POINTER(QmvEpilogue), _vp]
+_lib.qmv_matvec_ex.restype = _int
+_lib.qmv_matvec_swiglu.argtypes = [_int, _i64, _i64, _i64, _vp, _vp, _vp, _int, _vp, _int, _vp]
+_lib.qmv_matvec_swiglu.restype = _int
+
+
 class QmvMatvecItem(ctypes.Structure):
     _fields_ = [("N", ctypes.c_int64), ("W", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
                 ("fmt", ctypes.c_int32)]
@@ -89,7 +99,8 @@ _lib.qmv_dequant.argtypes = [_int, _i64, _i64, _vp, _vp, _vp]
 _lib.qmv_dequant.restype = _int
 
 EXPORTS = ("qmv_abi_version", "qmv_status_string", "qmv_last_error", "qmv_packed_bytes",
-           "qmv_pack", "qmv_matvec", "qmv_matvec_grouped", "qmv_gemm", "qmv_dequant")
+           "qmv_pack", "qmv_matvec", "qmv_matvec_ex", "qmv_matvec_swiglu", "qmv_matvec_grouped", "qmv_gemm",
+           "qmv_dequant")
 
 
 class QmvError(RuntimeError):
@@ -196,6 +207,53 @@ def matvec(fmt, W: torch.Tensor, x: torch.Tensor, N: int, K: int, y: torch.Tenso
     _check(_lib.qmv_matvec(_fmt(fmt), N, K, b, _ptr(W), _ptr(x2), _DTYPES[x2.dtype], _ptr(y),
                            _DTYPES[y.dtype], _stream(stream)))
     return y
+
+
+def matvec_ex(fmt, W: torch.Tensor, x: torch.Tensor, N: int, K: int, y: torch.Tensor | None = None,
+              bias: torch.Tensor | None = None, residual: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y [b][N] f32 = residual + (W x + bias): the bias / residual add fused into
+    the matvec.  bias f32 [N] or None; residual f32 [b][N] or None (may be y)."""
+    x2 = x if x.dim() == 2 else x.reshape(1, -1)
+    b = x2.shape[0]
+    if x2.shape[1] != K:
+        raise ValueError(f"x has {x2.shape[1]} columns, expected K={K}")
+    if y is None:
+        y = torch.empty((b, N), dtype=torch.float32, device=x.device)
+    if x2.dtype not in _DTYPES or y.dtype not in _DTYPES:
+        raise ValueError("x / y dtype must be float32, float16 or bfloat16")
+    _need(W, packed_bytes(fmt, N, K), "W")
+    _need(y, b * N * 4, "y")
+    ep = QmvEpilogue()
+    if bias is not None:
+        _need_dtype(bias, torch.float32, "bias")
+        _need(bias, N * 4, "bias")
+        ep.bias = _ptr(bias)
+    if residual is not None:
+        _need_dtype(residual, torch.float32, "residual")
+        _need(residual, b * N * 4, "residual")
+        ep.residual = _ptr(residual)
+    _check(_lib.qmv_matvec_ex(_fmt(fmt), N, K, b, _ptr(W), _ptr(x2), _DTYPES[x2.dtype], _ptr(y),
+                              _DTYPES[y.dtype], ctypes.byref(ep), _stream(stream)))
+    return y
+
+
+def matvec_swiglu(fmt, W_gate: torch.Tensor, W_up: torch.Tensor, x: torch.Tensor, N: int, K: int,
+                  h: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """h [b][N] f32 = silu(W_gate x) * (W_up x), gate / up / SwiGLU in one pass."""
+    x2 = x if x.dim() == 2 else x.reshape(1, -1)
+    b = x2.shape[0]
+    if x2.shape[1] != K:
+        raise ValueError(f"x has {x2.shape[1]} columns, expected K={K}")
+    if h is None:
+        h = torch.empty((b, N), dtype=torch.float32, device=x.device)
+    if x2.dtype not in _DTYPES or h.dtype not in _DTYPES:
+        raise ValueError("x / h dtype must be float32, float16 or bfloat16")
+    _need(W_gate, packed_bytes(fmt, N, K), "W_gate")
+    _need(W_up, packed_bytes(fmt, N, K), "W_up")
+    _need(h, b * N * 4, "h")
+    _check(_lib.qmv_matvec_swiglu(_fmt(fmt), N, K, b, _ptr(W_gate), _ptr(W_up), _ptr(x2), _DTYPES[x2.dtype],
+                                  _ptr(h), _DTYPES[h.dtype], _stream(stream)))
+    return h
 
 
 def matvec_grouped(fmt, items, K: int, stream=None) -> list:

@@ -204,6 +204,36 @@ int qmv_matvec(int fmt, int64_t N, int64_t K, int64_t batch, const void* W, cons
                   "matvec");
 }
 
+int qmv_matvec_ex(int fmt, int64_t N, int64_t K, int64_t batch, const void* W, const void* x, int x_dtype,
+                  void* y, int y_dtype, const qmv_epilogue* ep, void* stream) {
+  int st;
+  if ((st = check_fmt(fmt))) return st;
+  if ((st = check_matvec_args(fmt, N, K, batch, W, x, x_dtype, y, y_dtype, ""))) return st;
+  const float* bias = ep ? ep->bias : nullptr;
+  const float* res = ep ? ep->residual : nullptr;
+  if (bias && !aligned(bias, 4)) return fail(QMV_ERR_ALIGN, "ep->bias is not 4-byte aligned");
+  if (res && !aligned(res, 4)) return fail(QMV_ERR_ALIGN, "ep->residual is not 4-byte aligned");
+  if ((st = check_device())) return st;
+  return launched(qmv::launch_matvec_epi(fmt, N, K, batch, static_cast<const uint8_t*>(W), nullptr, x, x_dtype,
+                                         static_cast<float*>(y), bias, res, as_stream(stream)),
+                  "matvec_ex");
+}
+
+int qmv_matvec_swiglu(int fmt, int64_t N, int64_t K, int64_t batch, const void* W_gate, const void* W_up,
+                      const void* x, int x_dtype, void* h, int h_dtype, void* stream) {
+  int st;
+  if ((st = check_fmt(fmt))) return st;
+  if (!W_gate) return fail(QMV_ERR_NULL, "W_gate is NULL");
+  if (!W_up) return fail(QMV_ERR_NULL, "W_up is NULL");
+  if ((st = check_matvec_args(fmt, N, K, batch, W_gate, x, x_dtype, h, h_dtype, ""))) return st;
+  if (!aligned(W_up, 16)) return fail(QMV_ERR_ALIGN, "W_up is not 16-byte aligned");
+  if ((st = check_device())) return st;
+  return launched(qmv::launch_matvec_epi(fmt, N, K, batch, static_cast<const uint8_t*>(W_gate),
+                                         static_cast<const uint8_t*>(W_up), x, x_dtype, static_cast<float*>(h),
+                                         nullptr, nullptr, as_stream(stream)),
+                  "matvec_swiglu");
+}
+
 int qmv_matvec_grouped(int fmt, int64_t K, int64_t batch, int count, const qmv_matvec_item* items,
                        int x_dtype, int y_dtype, void* stream) {
   int st;

@@ -439,12 +439,24 @@ constexpr int kMix = 0;  // FMT of a table mixing Q4K and Q6K segments
 // launch: kernels take a table of capacity CAP = 1, 4 or 16, the smallest that
 // holds the launch's segments (MI355X, grouped 2 x 5632 x 2048 gate+up:
 // 5.13 us with a 16-entry table of 1.35 KB, 4.84 us with a 4-entry one).
+// Fused epilogue of a single-matrix launch (the pages' decode kernels take the
+// biases and the residual adds in their epilogues and run gate / up / SwiGLU
+// as one product: aot-llm README, Metal backend notes).  Grouped launches
+// leave every pointer null.
+struct Epi {
+  const uint8_t* W2;   // SwiGLU: the up matrix (same format, shape and planes as the gate)
+  const float* bias;   // [N] added to the product, or null
+  const float* res;    // [N] residual added last, or null (may be y itself)
+};
+
 template <int CAP>
 struct SegTableT {
   int first[CAP];  // first block of each segment (INT_MAX past count): one wide scalar load
   Seg s[CAP];
   int count;
   int K;
+  Epi ep;
+  int pair;        // host only: 1 launches the SwiGLU kernel (one segment, ep.W2 set)
 };
 using SegTable = SegTableT<kMaxSeg>;  // built on the host, then shrunk to the launch
 
@@ -457,6 +469,8 @@ SegTableT<CAP> shrink(const SegTable& t) {  // t.count <= CAP
   }
   o.count = t.count;
   o.K = t.K;
+  o.ep = t.ep;
+  o.pair = t.pair;
   return o;
 }
 
@@ -478,8 +492,15 @@ __device__ __forceinline__ void store_y(rsrc_t ry, int row, bool ok, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ry, int(ok ? uint32_t(row) * 4u : kOOB), 0, 0);
 }
 
-template <int FMT, bool XF16, int LPR, int UPL, int R, int KS, bool DB>
-__device__ __forceinline__ void xs_segment(const Seg& sg, const int K) {
+// PAIR: SwiGLU, h = silu(gate row . x) * (up row . x): every row group loads
+// the same rows of both matrices (ep.W2 is the up matrix) and the epilogue
+// combines the two totals.  Otherwise bias and residual (null: none) are
+// added to each total in the epilogue.
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+template <int FMT, bool XF16, int LPR, int UPL, int R, int KS, bool DB, bool PAIR = false>
+__device__ __forceinline__ void xs_segment(const Seg& sg, const int K, const Epi& ep) {
+  constexpr int NM = PAIR ? 2 : 1;           // matrices read per row group
   constexpr int TPB = KS == 1 ? kWaves : 1;  // independent lane-group teams per block
   constexpr int BT = 64 * (KS == 1 ? kWaves : KS);  // threads per block
   constexpr bool H2 = (FMT == QMV_W4A16_G64 && XF16);
@@ -490,7 +511,24 @@ __device__ __forceinline__ void xs_segment(const Seg& sg, const int K) {
   const int U = K >> 5;
   const Geo g{make_rsrc(sg.W, sg.nrec[0]), make_rsrc(sg.W + sg.off1, sg.nrec[1]),
               make_rsrc(sg.W + sg.off2, sg.nrec[2]), make_rsrc(sg.W + sg.off3, sg.nrec[3]), K};
+  [[maybe_unused]] Geo g2 = g;
+  if constexpr (PAIR)
+    g2 = Geo{make_rsrc(ep.W2, sg.nrec[0]), make_rsrc(ep.W2 + sg.off1, sg.nrec[1]),
+             make_rsrc(ep.W2 + sg.off2, sg.nrec[2]), make_rsrc(ep.W2 + sg.off3, sg.nrec[3]), K};
   const int N = sg.N;
+  // the value stored for row `row` from its total(s) (row is clamped for the
+  // epilogue loads; the store itself is predicated)
+  auto finish = [&](int row, float tot, float tot2) -> float {
+    if constexpr (PAIR) {
+      return silu_mul(tot, tot2);
+    } else {
+      const int rc = row < N ? row : N - 1;
+      float v = tot;
+      if (ep.bias) v += ep.bias[rc];
+      if (ep.res) v = ep.res[rc] + v;
+      return v;
+    }
+  };
   const rsrc_t ry = make_rsrc(sg.y, uint32_t(N) * 4u);
   const int ngroups = (N + R * RPW - 1) / (R * RPW);
   // wave-uniform (readfirstlane): the loop's branches and loads stay scalar-controlled
@@ -498,7 +536,7 @@ __device__ __forceinline__ void xs_segment(const Seg& sg, const int K) {
   const int gw = (int(blockIdx.x) - sg.b0) * TPB + (KS == 1 ? wv : 0);
   const int TW = sg.nb * TPB;
   const int ks = KS == 1 ? 0 : wv;  // K slice of this wave
-  __shared__ float red[2][KS][RPW * R];
+  __shared__ float red[2][KS][NM * RPW * R];
   int par = 0;
 
   int uu[UPL], sh[UPL];
@@ -542,14 +580,16 @@ __device__ __forceinline__ void xs_segment(const Seg& sg, const int K) {
   // 2. weights of this wave's first two row groups (one with DB = false):
   // both register sets in flight before anything waits (groups past the end
   // read nothing)
-  Raw<FMT> ga[R][UPL], gb[R][UPL];  // two register sets, used in turn (no copies)
-  auto load_group = [&](Raw<FMT> (&dst)[R][UPL], int gi) {
+  Raw<FMT> ga[NM][R][UPL], gb[NM][R][UPL];  // two register sets, used in turn (no copies)
+  auto load_group = [&](Raw<FMT> (&dst)[NM][R][UPL], int gi) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int row = gi * (R * RPW) + r * RPW + sub;
+    for (int m = 0; m < NM; ++m)
 #pragma unroll
-      for (int j = 0; j < UPL; ++j) dst[r][j] = load_raw<FMT>(g, row, uu[j], row < N && uv[j]);
-    }
+      for (int r = 0; r < R; ++r) {
+        const int row = gi * (R * RPW) + r * RPW + sub;
+#pragma unroll
+        for (int j = 0; j < UPL; ++j) dst[m][r][j] = load_raw<FMT>(m ? g2 : g, row, uu[j], row < N && uv[j]);
+      }
   };
   int grp = gw;
   load_group(ga, grp);
@@ -581,37 +621,49 @@ __device__ __forceinline__ void xs_segment(const Seg& sg, const int K) {
     for (int j = 0; j < UPL; ++j) load_x<FMT, XF16>(xs[j], nullptr, 0, uv[j], &xr[j]);
   }
 
-  auto do_group = [&](const Raw<FMT> (&cur)[R][UPL], int gi) {
-    float acc[R];
+  auto do_group = [&](const Raw<FMT> (&cur)[NM][R][UPL], int gi) {
+    float acc[NM][R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[m][r] = 0.0f;
 #pragma unroll
     for (int j = 0; j < UPL; ++j) {
       if (uv[j]) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) acc[r] = unit_dot<FMT, XF16>(cur[r][j], xs[j], sh[j], acc[r]);
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int r = 0; r < R; ++r) acc[m][r] = unit_dot<FMT, XF16>(cur[m][r][j], xs[j], sh[j], acc[m][r]);
       }
     }
     if constexpr (LPR == 64 && (R == 1 || R == 2 || R == 4)) {
       // one row per lane range: lane l holds row r = l / (64 / R)
-      const float tot = wave_rows_sum<R>(acc);
+      const float tot = wave_rows_sum<R>(acc[0]);
+      const float tot2 = PAIR ? wave_rows_sum<R>(acc[NM - 1]) : 0.0f;
       const int r = lane / (64 / R);
       const bool first = lane % (64 / R) == 0;
       const int row = gi * R + r;
       if constexpr (KS == 1) {
-        store_y(ry, row, first && row < N, tot);
+        store_y(ry, row, first && row < N, finish(row, tot, tot2));
       } else {
-        if (first) red[par][ks][r] = tot;
+        if (first) {
+          red[par][ks][r] = tot;
+          if constexpr (PAIR) red[par][ks][RPW * R + r] = tot2;
+        }
       }
     } else {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const float tot = group_sum<LPR>(acc[r], sub);
+        const float tot = group_sum<LPR>(acc[0][r], sub);
+        const float tot2 = PAIR ? group_sum<LPR>(acc[NM - 1][r], sub) : 0.0f;
         const int row = gi * (R * RPW) + r * RPW + sub;
         if constexpr (KS == 1) {
-          store_y(ry, row, l == 0 && row < N, tot);
+          store_y(ry, row, l == 0 && row < N, finish(row, tot, tot2));
         } else {
-          if (l == 0) red[par][ks][r * RPW + sub] = tot;
+          if (l == 0) {
+            red[par][ks][r * RPW + sub] = tot;
+            if constexpr (PAIR) red[par][ks][RPW * R + r * RPW + sub] = tot2;
+          }
         }
       }
     }
@@ -620,10 +672,13 @@ __device__ __forceinline__ void xs_segment(const Seg& sg, const int K) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int row = gi * (R * RPW) + r * RPW + sub;
-        float t = 0.0f;
+        float t = 0.0f, t2 = 0.0f;
 #pragma unroll
-        for (int w = 0; w < KS; ++w) t += red[par][w][r * RPW + sub];
-        store_y(ry, row, ks == 0 && l == 0 && row < N, t);
+        for (int w = 0; w < KS; ++w) {
+          t += red[par][w][r * RPW + sub];
+          if constexpr (PAIR) t2 += red[par][w][RPW * R + r * RPW + sub];
+        }
+        store_y(ry, row, ks == 0 && l == 0 && row < N, finish(row, t, t2));
       }
       par ^= 1;  // the next group writes the other buffer while this one is read
     }
@@ -657,7 +712,13 @@ __global__ __launch_bounds__(KS == 1 ? kThreads : 64 * KS) void matvec_xs_kernel
 #pragma unroll
     for (int i = 1; i < CAP; ++i) si += int(blockIdx.x) >= t.first[i] ? 1 : 0;
   }
-  xs_segment<FMT, XF16, LPR, UPL, R, KS, DB>(t.s[si], t.K);
+  xs_segment<FMT, XF16, LPR, UPL, R, KS, DB>(t.s[si], t.K, t.ep);
+}
+
+// SwiGLU of one gate / up pair: one segment (the gate), ep.W2 the up matrix.
+template <int FMT, bool XF16, int LPR, int UPL, int R, int KS, bool DB>
+__global__ __launch_bounds__(KS == 1 ? kThreads : 64 * KS) void matvec_xs_pair_kernel(const SegTableT<1> t) {
+  xs_segment<FMT, XF16, LPR, UPL, R, KS, DB, true>(t.s[0], t.K, t.ep);
 }
 
 // Q4K and Q6K segments in one launch (the K-quant mix of one decoder layer's
@@ -668,8 +729,8 @@ __global__ __launch_bounds__(KS == 1 ? kThreads : 64 * KS) void matvec_xs_mix_ke
 #pragma unroll
   for (int i = 1; i < CAP; ++i) si += int(blockIdx.x) >= t.first[i] ? 1 : 0;
   const Seg& sg = t.s[si];
-  if (sg.fmt == QMV_Q6K) xs_segment<QMV_Q6K, false, LPR, UPL, R, KS, DB>(sg, t.K);
-  else xs_segment<QMV_Q4K, false, LPR, UPL, R, KS, DB>(sg, t.K);
+  if (sg.fmt == QMV_Q6K) xs_segment<QMV_Q6K, false, LPR, UPL, R, KS, DB>(sg, t.K, t.ep);
+  else xs_segment<QMV_Q4K, false, LPR, UPL, R, KS, DB>(sg, t.K, t.ep);
 }
 
 bool double_buffer_forced() {
@@ -724,7 +785,11 @@ hipError_t go(SegTable& t, hipStream_t s) {
       else
         hipLaunchKernelGGL((matvec_xs_mix_kernel<LPR, UPL, R, KS, DB, kMaxSeg>), grid, block, 0, s, t);
     } else {
-      if (t.count == 1)
+      if (t.pair) {
+        // two matrices' registers per row group: at most two rows x units per lane
+        if constexpr (R * UPL <= 2)
+          hipLaunchKernelGGL((matvec_xs_pair_kernel<FMT, XF16, LPR, UPL, R, KS, DB>), grid, block, 0, s, shrink<1>(t));
+      } else if (t.count == 1)
         hipLaunchKernelGGL((matvec_xs_kernel<FMT, XF16, LPR, UPL, R, 1, KS, DB>), grid, block, 0, s, shrink<1>(t));
       else if (t.count <= 4)
         hipLaunchKernelGGL((matvec_xs_kernel<FMT, XF16, LPR, UPL, R, 4, KS, DB>), grid, block, 0, s, shrink<4>(t));
@@ -758,12 +823,15 @@ hipError_t pick_r(SegTable& t, int rsel, hipStream_t s) {
   const bool four_fits = KS == 1 && LPR == 64 && rows / 2 > 256 * 16 && (rows + 3) / 4 <= 256 * 16;
   int r = rsel ? rsel : slots <= 1024 ? 1 : ((H2 && KS == 1) || four_fits) ? 4 : 2;
   if constexpr (FMT == QMV_DENSE_BF16) r = r > 2 ? 2 : r;  // 16 weight registers per unit and row
+  if (t.pair) r = UPL >= 2 ? 1 : (r > 2 ? 2 : r);          // SwiGLU: two matrices' registers
   if constexpr (H2 && KS == 1 && UPL == 1) {
     if (r == 8) return go<FMT, XF16, LPR, UPL, 8, KS>(t, s);
   } else {
     r = r == 8 ? 4 : r;
   }
-  if (r == 4) return go<FMT, XF16, LPR, UPL, 4, KS>(t, s);
+  if constexpr (FMT != QMV_DENSE_BF16) {
+    if (r == 4) return go<FMT, XF16, LPR, UPL, 4, KS>(t, s);
+  }
   return r == 2 ? go<FMT, XF16, LPR, UPL, 2, KS>(t, s) : go<FMT, XF16, LPR, UPL, 1, KS>(t, s);
 }
 
@@ -878,11 +946,21 @@ Seg make_seg(int fmt, int64_t N, int64_t K, const void* W, const void* x, void* 
 // uses the general kernel.
 bool launch_matvec_b1(int fmt, int64_t N, int64_t K, const uint8_t* W, const void* x, int x_dtype,
                       float* y, hipStream_t s, hipError_t* err) {
+  return launch_matvec_b1_epi(fmt, N, K, W, nullptr, x, x_dtype, y, nullptr, nullptr, s, err);
+}
+
+// The same with a fused epilogue: W2 != null runs SwiGLU (y = silu(W x) * (W2 x)),
+// otherwise bias / res (null: none) are added to the products.
+bool launch_matvec_b1_epi(int fmt, int64_t N, int64_t K, const uint8_t* W, const uint8_t* W2, const void* x,
+                          int x_dtype, float* y, const float* bias, const float* res, hipStream_t s,
+                          hipError_t* err) {
   if (!planes_fit(planes_of(fmt, N, K))) return false;
   SegTable t{};
   t.count = 1;
   t.K = int(K);
   t.s[0] = make_seg(fmt, N, K, W, x, y);
+  t.ep = Epi{W2, bias, res};
+  t.pair = W2 != nullptr;
   return launch_table(fmt, t, x_dtype, s, err);
 }
 

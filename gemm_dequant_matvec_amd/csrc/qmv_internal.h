@@ -131,6 +131,12 @@ hipError_t launch_matvec(int fmt, int64_t N, int64_t K, int64_t batch, const uin
                          const void* x, int x_dtype, float* y, hipStream_t s);
 bool launch_matvec_b1(int fmt, int64_t N, int64_t K, const uint8_t* W, const void* x, int x_dtype,
                       float* y, hipStream_t s, hipError_t* err);
+bool launch_matvec_b1_epi(int fmt, int64_t N, int64_t K, const uint8_t* W, const uint8_t* W2, const void* x,
+                          int x_dtype, float* y, const float* bias, const float* res, hipStream_t s,
+                          hipError_t* err);
+hipError_t launch_matvec_epi(int fmt, int64_t N, int64_t K, int64_t batch, const uint8_t* W, const uint8_t* W2,
+                             const void* x, int x_dtype, float* y, const float* bias, const float* res,
+                             hipStream_t s);
 bool launch_matvec_mfma(int fmt, int64_t N, int64_t K, int nv, const uint8_t* W, const void* x, int x_dtype,
                         float* y, hipStream_t s, hipError_t* err);
 bool launch_matvec_grouped_mfma(int fmt, int64_t K, int64_t batch, int count, const qmv_matvec_item* items,

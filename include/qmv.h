@@ -222,6 +222,39 @@ int qmv_pack(int fmt, int64_t N, int64_t K, int64_t batch, const qmv_logical* sr
 int qmv_matvec(int fmt, int64_t N, int64_t K, int64_t batch, const void* W,
                const void* x, int x_dtype, void* y, int y_dtype, void* stream);
 
+/* Fused epilogue of qmv_matvec_ex (all device pointers, f32, 4-byte aligned). */
+typedef struct qmv_epilogue {
+  const float* bias;      /* [N] added to every vector's product, or NULL */
+  const float* residual;  /* [batch][N] added last, or NULL; may be y itself (y += W x) but
+                             must not otherwise overlap y */
+} qmv_epilogue;
+
+/*
+ * y[b][n] = residual[b][n] + (sum_k W[n][k] * x[b][k] + bias[n]), the bias and
+ * residual adds fused into the matvec's epilogue (aot-llm README, Metal
+ * backend notes: the q / k / v kernels add their biases in the epilogue, wo
+ * and down fuse the residual add).  ep == NULL, or both pointers NULL, is
+ * qmv_matvec.  Arguments otherwise as qmv_matvec.  The epilogue adds two f32
+ * roundings to the matvec tolerance.  Batch 2..8 with an epilogue runs on the
+ * FMA kernel (the matrix-core kernel has none).
+ * Errors: as qmv_matvec, plus ALIGN for a misaligned bias / residual.
+ */
+int qmv_matvec_ex(int fmt, int64_t N, int64_t K, int64_t batch, const void* W, const void* x, int x_dtype,
+                  void* y, int y_dtype, const qmv_epilogue* ep, void* stream);
+
+/*
+ * h[b][n] = silu(g) * u with g = sum_k Wg[n][k] x[b][k], u = sum_k Wu[n][k] x[b][k]
+ * and silu(z) = z / (1 + exp(-z)): the gate / up projections and the SwiGLU
+ * product in one pass (aot-llm README, Metal backend notes: the fused
+ * gate / up / SwiGLU product).  W_gate and W_up are packed matrices of the
+ * same format and shape; each row of both is read once, and only h is
+ * written.  x, h and dtypes as qmv_matvec (h is y).  Tolerance: the matvec
+ * bound of g and u propagated through silu (Lipschitz 1.1) and the product.
+ * Errors: as qmv_matvec (NULL names W_gate or W_up).
+ */
+int qmv_matvec_swiglu(int fmt, int64_t N, int64_t K, int64_t batch, const void* W_gate, const void* W_up,
+                      const void* x, int x_dtype, void* h, int h_dtype, void* stream);
+
 /*
  * Several matvecs of one K and one batch in as few launches as possible: for
  * every item i, y_i[b][n] = sum_k W_i[n][k] * x_i[b][k].

@@ -30,7 +30,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
         ["qmv_abi_version", "qmv_status_string", "qmv_last_error", "qmv_packed_bytes",
-         "qmv_pack", "qmv_matvec", "qmv_matvec_grouped", "qmv_gemm", "qmv_dequant"])
+         "qmv_pack", "qmv_matvec", "qmv_matvec_ex", "qmv_matvec_swiglu", "qmv_matvec_grouped", "qmv_gemm",
+         "qmv_dequant"])
 
 
 def test_library_exports_every_declared_symbol(q):
@@ -147,3 +148,25 @@ def test_grouped_item_format_errors(q):
     assert "items[0]" in q.last_error()
     assert call(0, 64, 1, 3, items, 1, 1, None) == -4  # K = 64 is no Q4K block multiple
     assert "Q4K" in q.last_error() or "q4k" in q.last_error().lower()
+
+
+def test_epilogue_and_swiglu_argument_errors(q):
+    P = 1 << 20
+    ep = q.QmvEpilogue()
+    ex = lambda *a: q.raw_call("qmv_matvec_ex", *a)  # noqa: E731
+    sw = lambda *a: q.raw_call("qmv_matvec_swiglu", *a)  # noqa: E731
+    ep.bias = P + 2
+    assert ex(3, 64, 256, 1, P, P, 1, P, 1, ctypes.byref(ep), None) == -5
+    assert "bias" in q.last_error()
+    ep.bias, ep.residual = P, P + 1
+    assert ex(3, 64, 256, 1, P, P, 1, P, 1, ctypes.byref(ep), None) == -5
+    assert "residual" in q.last_error()
+    assert ex(3, 64, 200, 1, P, P, 1, P, 1, None, None) == -4    # K not a Q4K block multiple
+    assert ex(11, 64, 256, 1, P, P, 1, P, 1, None, None) == -2   # no such format
+    assert sw(3, 64, 256, 1, None, P, P, 1, P, 1, None) == -1
+    assert "W_gate" in q.last_error()
+    assert sw(3, 64, 256, 1, P, None, P, 1, P, 1, None) == -1
+    assert "W_up" in q.last_error()
+    assert sw(3, 64, 256, 1, P, P + 8, P, 1, P, 1, None) == -5
+    assert "W_up" in q.last_error()
+    assert sw(3, 64, 256, 1, P, P, P, 2, P, 1, None) == -3      # f16 x for Q4K
