@@ -25,6 +25,7 @@ Modules:
   reference  f64 matvec / GEMM, the per-output tolerance bound, and the fused
              decode epilogues (bias / residual add, SwiGLU) with their bounds
   layout     reference packer / unpacker of the library's packed layout v1
+  q8act      activations quantized to 8-bit blocks (the integer-dot variant)
 
 Parity status: every function here is pinned by `-m "not gpu"` tests against
 hand-worked blocks, library routines and exact rational arithmetic.
@@ -34,3 +35,4 @@ from .dequantize import dequant, dequant_rows  # noqa: F401
 from .reference import matvec_ref, gemm_ref, tolerance_bound, check_within  # noqa: F401
 from .reference import silu_ref, swiglu_ref, swiglu_bound, epilogue_ref, epilogue_bound  # noqa: F401
 from .layout import pack_ref, unpack_ref, packed_bytes_ref  # noqa: F401
+from .q8act import quantize_q8x, dequant_q8x, pack_q8x, q8x_record_bytes  # noqa: F401
