@@ -11,9 +11,13 @@ x[32j .. 32j + 31] (f32):
 
     amax = max_k |x_k|
     d    = amax / 127           (f32 division, round to nearest even)
-    id   = 127 / amax           (f32 division; 0 when amax = 0)
+    id   = 127 / amax           (f32 division)
     q_k  = rint(x_k * id)       (f32 product, then round half to even to an
                                  integer), clamped to [-127, 127]
+
+except that a block with amax < 2^-120 (all zero, or so small that 127 / amax
+would overflow f32 near amax = 3.7e-37) takes d = id = 0 and all codes 0: it
+quantizes to exact zeros.  Inputs must be finite.
 
 and the quantized activation is x^_k = d * q_k, exactly (an f64 product).
 Every step is one IEEE f32 operation, so the codes and scales are unique bit
@@ -34,9 +38,10 @@ def quantize_q8x(x) -> tuple[np.ndarray, np.ndarray]:
         raise ValueError("K must be a multiple of 32")
     blocks = x.reshape(b, K // 32, 32)
     amax = np.max(np.abs(blocks), axis=2)                      # exact
-    d = (amax / np.float32(127.0)).astype(np.float32)          # one f32 division
-    with np.errstate(divide="ignore"):
-        id_ = np.where(amax > 0, np.float32(127.0) / amax, np.float32(0.0)).astype(np.float32)
+    live = amax >= np.float32(2.0 ** -120)
+    with np.errstate(divide="ignore", over="ignore"):
+        d = np.where(live, amax / np.float32(127.0), np.float32(0.0)).astype(np.float32)    # one f32 division
+        id_ = np.where(live, np.float32(127.0) / amax, np.float32(0.0)).astype(np.float32)  # one f32 division
     prod = (blocks * id_[:, :, None]).astype(np.float32)       # one f32 product
     q = np.clip(np.rint(prod), -127, 127).astype(np.int8)      # round half to even
     return q.reshape(b, K), d

@@ -97,3 +97,17 @@ def test_mutations_are_caught():
         assert not pins_hold(m), m.__name__
     two = np.concatenate([_x("q8x_ramp"), _x("q8x_halfway")], axis=1)
     assert not np.array_equal(per_vector(two)[1], oracle.quantize_q8x(two)[1])
+
+
+def test_tiny_blocks_quantize_to_zero():
+    # 127 / amax overflows f32 below amax ~ 3.7e-37: such a block (threshold
+    # 2^-120) quantizes to exact zeros; at the threshold itself id = 127 * 2^120
+    # is exact and a half-way product rounds to even.
+    x = np.zeros((1, 64), np.float32)
+    x[0, 0], x[0, 1] = 1e-37, -5e-38
+    x[0, 32], x[0, 33] = 2.0 ** -120, -(2.0 ** -121)
+    q, d = oracle.quantize_q8x(x)
+    assert not np.any(q[0, :32]) and d[0, 0] == 0.0
+    assert q[0, 32] == 127 and q[0, 33] == -64 and not np.any(q[0, 34:])
+    assert d[0, 1] == np.float32(2.0 ** -120) / np.float32(127)
+    assert np.all(np.isfinite(oracle.dequant_q8x(q, d)))
