@@ -93,6 +93,10 @@ class QmvMatvecItem(ctypes.Structure):
 
 _lib.qmv_matvec_grouped.argtypes = [_int, _i64, _i64, _int, ctypes.POINTER(QmvMatvecItem), _int, _int, _vp]
 _lib.qmv_matvec_grouped.restype = _int
+_lib.qmv_quantize_x.argtypes = [_i64, _i64, _vp, _vp, _vp]
+_lib.qmv_quantize_x.restype = _int
+_lib.qmv_q8x_bytes.argtypes = [_i64, _i64, ctypes.POINTER(ctypes.c_size_t)]
+_lib.qmv_q8x_bytes.restype = _int
 _lib.qmv_gemm.argtypes = [_int, _i64, _i64, _i64, _vp, _vp, _int, _vp, _int, _vp]
 _lib.qmv_gemm.restype = _int
 _lib.qmv_dequant.argtypes = [_int, _i64, _i64, _vp, _vp, _vp]
@@ -100,7 +104,7 @@ _lib.qmv_dequant.restype = _int
 
 EXPORTS = ("qmv_abi_version", "qmv_status_string", "qmv_last_error", "qmv_packed_bytes",
            "qmv_pack", "qmv_matvec", "qmv_matvec_ex", "qmv_matvec_swiglu", "qmv_matvec_grouped", "qmv_gemm",
-           "qmv_dequant")
+           "qmv_dequant", "qmv_quantize_x", "qmv_q8x_bytes")
 
 
 class QmvError(RuntimeError):
@@ -191,36 +195,76 @@ def pack(fmt, logical: dict, N: int | None = None, K: int | None = None, batch: 
     return out
 
 
-def matvec(fmt, W: torch.Tensor, x: torch.Tensor, N: int, K: int, y: torch.Tensor | None = None,
-           stream=None) -> torch.Tensor:
-    """y [b][N] f32 = W x for x [b][K] (f32, or f16 for w4a16_g64)."""
+class Q8X:
+    """Activations quantized to 8-bit blocks by quantize_x: `data` is the
+    device buffer (uint8), `K` and `batch` its shape."""
+
+    def __init__(self, data: torch.Tensor, K: int, batch: int):
+        self.data, self.K, self.batch = data, K, batch
+
+
+def q8x_bytes(K: int, batch: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(_lib.qmv_q8x_bytes(K, batch, ctypes.byref(out)))
+    return out.value
+
+
+def quantize_x(x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> Q8X:
+    """f32 x [b][K] -> Q8X (per 32 activations: 8-bit codes and an f32 scale)."""
     x2 = x if x.dim() == 2 else x.reshape(1, -1)
-    b = x2.shape[0]
+    b, K = x2.shape
+    nbytes = q8x_bytes(K, b)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    _need_dtype(x2, torch.float32, "x")
+    _need(out, nbytes, "out")
+    _check(_lib.qmv_quantize_x(K, b, _ptr(x2), _ptr(out), _stream(stream)))
+    return Q8X(out, K, b)
+
+
+def _xarg(x, K: int):
+    """(pointer, dtype code, batch) of an activation argument: a tensor [b][K]
+    (f32 / f16) or a Q8X."""
+    if isinstance(x, Q8X):
+        if x.K != K:
+            raise ValueError(f"Q8X activations have K={x.K}, expected K={K}")
+        _need(x.data, q8x_bytes(K, x.batch), "x")
+        return _ptr(x.data), 4, x.batch, x.data.device
+    x2 = x if x.dim() == 2 else x.reshape(1, -1)
     if x2.shape[1] != K:
         raise ValueError(f"x has {x2.shape[1]} columns, expected K={K}")
+    if x2.dtype not in _DTYPES:
+        raise ValueError("x dtype must be float32, float16 or bfloat16")
+    return _ptr(x2), _DTYPES[x2.dtype], x2.shape[0], x2.device
+
+
+def matvec(fmt, W: torch.Tensor, x, N: int, K: int, y: torch.Tensor | None = None,
+           stream=None) -> torch.Tensor:
+    """y [b][N] f32 = W x for x [b][K] (f32, f16 for w4a16_g64, or a Q8X from quantize_x)."""
+    b = x.batch if isinstance(x, Q8X) else (x.shape[0] if x.dim() == 2 else 1)
+    dev = x.data.device if isinstance(x, Q8X) else x.device
     if y is None:
-        y = torch.empty((b, N), dtype=torch.float32, device=x.device)
-    if x2.dtype not in _DTYPES or y.dtype not in _DTYPES:
-        raise ValueError("x / y dtype must be float32, float16 or bfloat16")
+        y = torch.empty((b, N), dtype=torch.float32, device=dev)
+    if y.dtype not in _DTYPES:
+        raise ValueError("y dtype must be float32, float16 or bfloat16")
     _need(W, packed_bytes(fmt, N, K), "W")
     _need(y, b * N * 4, "y")
-    _check(_lib.qmv_matvec(_fmt(fmt), N, K, b, _ptr(W), _ptr(x2), _DTYPES[x2.dtype], _ptr(y),
-                           _DTYPES[y.dtype], _stream(stream)))
+    xp, xdt, b, _ = _xarg(x, K)
+    _check(_lib.qmv_matvec(_fmt(fmt), N, K, b, _ptr(W), xp, xdt, _ptr(y), _DTYPES[y.dtype], _stream(stream)))
     return y
 
 
 def matvec_ex(fmt, W: torch.Tensor, x: torch.Tensor, N: int, K: int, y: torch.Tensor | None = None,
               bias: torch.Tensor | None = None, residual: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """y [b][N] f32 = residual + (W x + bias): the bias / residual add fused into
-    the matvec.  bias f32 [N] or None; residual f32 [b][N] or None (may be y)."""
-    x2 = x if x.dim() == 2 else x.reshape(1, -1)
-    b = x2.shape[0]
-    if x2.shape[1] != K:
-        raise ValueError(f"x has {x2.shape[1]} columns, expected K={K}")
+    the matvec.  bias f32 [N] or None; residual f32 [b][N] or None (may be y).
+    x as in matvec."""
+    b = x.batch if isinstance(x, Q8X) else (x.shape[0] if x.dim() == 2 else 1)
+    dev = x.data.device if isinstance(x, Q8X) else x.device
     if y is None:
-        y = torch.empty((b, N), dtype=torch.float32, device=x.device)
-    if x2.dtype not in _DTYPES or y.dtype not in _DTYPES:
-        raise ValueError("x / y dtype must be float32, float16 or bfloat16")
+        y = torch.empty((b, N), dtype=torch.float32, device=dev)
+    if y.dtype not in _DTYPES:
+        raise ValueError("y dtype must be float32, float16 or bfloat16")
     _need(W, packed_bytes(fmt, N, K), "W")
     _need(y, b * N * 4, "y")
     ep = QmvEpilogue()
@@ -232,26 +276,27 @@ def matvec_ex(fmt, W: torch.Tensor, x: torch.Tensor, N: int, K: int, y: torch.Te
         _need_dtype(residual, torch.float32, "residual")
         _need(residual, b * N * 4, "residual")
         ep.residual = _ptr(residual)
-    _check(_lib.qmv_matvec_ex(_fmt(fmt), N, K, b, _ptr(W), _ptr(x2), _DTYPES[x2.dtype], _ptr(y),
+    xp, xdt, b, _ = _xarg(x, K)
+    _check(_lib.qmv_matvec_ex(_fmt(fmt), N, K, b, _ptr(W), xp, xdt, _ptr(y),
                               _DTYPES[y.dtype], ctypes.byref(ep), _stream(stream)))
     return y
 
 
 def matvec_swiglu(fmt, W_gate: torch.Tensor, W_up: torch.Tensor, x: torch.Tensor, N: int, K: int,
                   h: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """h [b][N] f32 = silu(W_gate x) * (W_up x), gate / up / SwiGLU in one pass."""
-    x2 = x if x.dim() == 2 else x.reshape(1, -1)
-    b = x2.shape[0]
-    if x2.shape[1] != K:
-        raise ValueError(f"x has {x2.shape[1]} columns, expected K={K}")
+    """h [b][N] f32 = silu(W_gate x) * (W_up x), gate / up / SwiGLU in one pass
+    (x as in matvec)."""
+    b = x.batch if isinstance(x, Q8X) else (x.shape[0] if x.dim() == 2 else 1)
+    dev = x.data.device if isinstance(x, Q8X) else x.device
     if h is None:
-        h = torch.empty((b, N), dtype=torch.float32, device=x.device)
-    if x2.dtype not in _DTYPES or h.dtype not in _DTYPES:
-        raise ValueError("x / h dtype must be float32, float16 or bfloat16")
+        h = torch.empty((b, N), dtype=torch.float32, device=dev)
+    if h.dtype not in _DTYPES:
+        raise ValueError("h dtype must be float32, float16 or bfloat16")
     _need(W_gate, packed_bytes(fmt, N, K), "W_gate")
     _need(W_up, packed_bytes(fmt, N, K), "W_up")
     _need(h, b * N * 4, "h")
-    _check(_lib.qmv_matvec_swiglu(_fmt(fmt), N, K, b, _ptr(W_gate), _ptr(W_up), _ptr(x2), _DTYPES[x2.dtype],
+    xp, xdt, b, _ = _xarg(x, K)
+    _check(_lib.qmv_matvec_swiglu(_fmt(fmt), N, K, b, _ptr(W_gate), _ptr(W_up), xp, xdt,
                                   _ptr(h), _DTYPES[h.dtype], _stream(stream)))
     return h
 
@@ -260,22 +305,31 @@ def matvec_grouped(fmt, items, K: int, stream=None) -> list:
     """Several matvecs of one K in as few launches as possible.
 
     items: sequence of (W, x, N), (W, x, N, y) or (W, x, N, y, item_fmt); x
-    [b][K] (same b and dtype for all), y allocated as f32 [b][N] when absent or
-    None; item_fmt overrides fmt for that matrix (fmt may then be None).
-    Returns the list of y.
+    [b][K] (same b and dtype for all) or a Q8X of b vectors (then for all), y
+    allocated as f32 [b][N] when absent or None; item_fmt overrides fmt for
+    that matrix (fmt may then be None).  Returns the list of y.
     """
     arr = (QmvMatvecItem * len(items))()
     outs, rows = [], []
     b = xdt = None
     for i, it in enumerate(items):  # every size check before any pointer is taken
         W, x, N = it[0], it[1], it[2]
-        x2 = x if x.dim() == 2 else x.reshape(1, -1)
+        if isinstance(x, Q8X):
+            if x.K != K:
+                raise ValueError(f"items[{i}]: Q8X activations have K={x.K}, expected K={K}")
+            _need(x.data, q8x_bytes(K, x.batch), f"items[{i}].x")
+            x2, shape, dt, device = x.data, (x.batch, K), "q8x", x.data.device
+        else:
+            x2 = x if x.dim() == 2 else x.reshape(1, -1)
+            shape, dt, device = tuple(x2.shape), x2.dtype, x.device
+            if dt not in _DTYPES:
+                raise ValueError("x dtype must be float32, float16 or bfloat16")
         if b is None:
-            b, xdt = x2.shape[0], x2.dtype
-        if x2.shape != (b, K) or x2.dtype != xdt:
+            b, xdt = shape[0], dt
+        if shape != (b, K) or dt != xdt:
             raise ValueError("all items need x of shape [b][K] and one dtype")
         y = it[3] if len(it) > 3 and it[3] is not None else torch.empty((b, N), dtype=torch.float32,
-                                                                          device=x.device)
+                                                                          device=device)
         ifmt = it[4] if len(it) > 4 and it[4] is not None else fmt
         if ifmt is None:
             raise ValueError(f"item {i} names no format and the call's fmt is None")
@@ -286,7 +340,8 @@ def matvec_grouped(fmt, items, K: int, stream=None) -> list:
     for i, (W, x2, N, y, ifmt) in enumerate(rows):
         arr[i].N, arr[i].W, arr[i].x, arr[i].y = N, _ptr(W), _ptr(x2), _ptr(y)
         arr[i].fmt = _fmt(ifmt) if ifmt is not None else 0
-    _check(_lib.qmv_matvec_grouped(0 if fmt is None else _fmt(fmt), K, b, len(items), arr, _DTYPES[xdt],
+    _check(_lib.qmv_matvec_grouped(0 if fmt is None else _fmt(fmt), K, b, len(items), arr,
+                                   4 if xdt == "q8x" else _DTYPES[xdt],
                                    _DTYPES[torch.float32], _stream(stream)))
     return outs
 

@@ -177,13 +177,14 @@ static int check_matvec_args(int fmt, int64_t N, int64_t K, int64_t batch, const
   if (!W) return fail(QMV_ERR_NULL, "%sW is NULL", who);
   if (!x) return fail(QMV_ERR_NULL, "%sx is NULL", who);
   if (!y) return fail(QMV_ERR_NULL, "%sy is NULL", who);
-  if (x_dtype != QMV_F32 && x_dtype != QMV_F16 && x_dtype != QMV_BF16)
+  if (x_dtype != QMV_F32 && x_dtype != QMV_F16 && x_dtype != QMV_BF16 && x_dtype != QMV_Q8X)
     return fail(QMV_ERR_DTYPE, "x_dtype=%d is not a qmv_dtype", x_dtype);
-  if (y_dtype != QMV_F32 && y_dtype != QMV_F16 && y_dtype != QMV_BF16)
+  if (y_dtype != QMV_F32 && y_dtype != QMV_F16 && y_dtype != QMV_BF16 && y_dtype != QMV_Q8X)
     return fail(QMV_ERR_DTYPE, "y_dtype=%d is not a qmv_dtype", y_dtype);
-  if (x_dtype == QMV_BF16 || (x_dtype == QMV_F16 && fmt != QMV_W4A16_G64))
+  if (x_dtype == QMV_BF16 || (x_dtype == QMV_F16 && fmt != QMV_W4A16_G64) ||
+      (x_dtype == QMV_Q8X && fmt == QMV_DENSE_BF16))
     return fail(QMV_ERR_UNSUPPORTED, "%s%s matvec takes x as f32%s", who, fmt_name(fmt),
-                fmt == QMV_W4A16_G64 ? " or f16" : "");
+                fmt == QMV_W4A16_G64 ? ", f16 or Q8X" : fmt == QMV_DENSE_BF16 ? "" : " or Q8X");
   if (y_dtype != QMV_F32) return fail(QMV_ERR_UNSUPPORTED, "matvec writes y as f32 only");
   if (!aligned(W, 16)) return fail(QMV_ERR_ALIGN, "%sW is not 16-byte aligned", who);
   if (!aligned(x, 16)) return fail(QMV_ERR_ALIGN, "%sx is not 16-byte aligned", who);
@@ -292,6 +293,31 @@ int qmv_gemm(int fmt, int64_t N, int64_t K, int64_t M, const void* W, const void
                                    static_cast<const uint16_t*>(X), static_cast<uint16_t*>(Y),
                                    as_stream(stream)),
                   "gemm");
+}
+
+int qmv_q8x_bytes(int64_t K, int64_t batch, size_t* out_bytes) {
+  if (K < 32 || K % 32) return fail(QMV_ERR_SHAPE, "K=%lld must be a positive multiple of 32", (long long)K);
+  if (batch < 1) return fail(QMV_ERR_SHAPE, "batch=%lld must be >= 1", (long long)batch);
+  if (!out_bytes) return fail(QMV_ERR_NULL, "out_bytes is NULL");
+  if (K >= (int64_t(1) << 31) || batch > (int64_t(1) << 40) / qmv::q8x_record_bytes(K))
+    return fail(QMV_ERR_OVERFLOW, "batch * K too large");
+  *out_bytes = static_cast<size_t>(batch * qmv::q8x_record_bytes(K));
+  return ok();
+}
+
+int qmv_quantize_x(int64_t K, int64_t batch, const float* x, void* xq, void* stream) {
+  int st;
+  size_t bytes = 0;
+  if ((st = qmv_q8x_bytes(K, batch, &bytes))) return st;
+  if (!x) return fail(QMV_ERR_NULL, "x is NULL");
+  if (!xq) return fail(QMV_ERR_NULL, "xq is NULL");
+  if (!aligned(x, 16)) return fail(QMV_ERR_ALIGN, "x is not 16-byte aligned");
+  if (!aligned(xq, 16)) return fail(QMV_ERR_ALIGN, "xq is not 16-byte aligned");
+  if (batch * (K / 32) >= (int64_t(1) << 31) * 256)
+    return fail(QMV_ERR_OVERFLOW, "too many blocks for one launch");
+  if ((st = check_device())) return st;
+  return launched(qmv::launch_quantize_x(K, batch, x, static_cast<uint8_t*>(xq), as_stream(stream)),
+                  "quantize_x");
 }
 
 int qmv_dequant(int fmt, int64_t N, int64_t K, const void* W, float* out, void* stream) {

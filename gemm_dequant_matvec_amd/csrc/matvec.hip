@@ -80,7 +80,10 @@ struct Pow2Ceil {
 // PAIR: SwiGLU, y = silu(W x) * (W2 x) (W2 the up matrix, same format and
 // shape); otherwise bias [N] and res [nb][N] (null: none) are added in the
 // epilogue: y = res + (W x + bias).
-template <int FMT, bool XF16, int LPR, int B, int R, bool PAIR = false>
+// XQ8: x is a QMV_Q8X buffer (8-bit codes and an f32 scale per 32 activations):
+// every 32-weight unit is one or two integer dot products (v_dot4_i32_i8,
+// exact in int32) scaled back in f32.
+template <int FMT, bool XF16, int LPR, int B, int R, bool PAIR = false, bool XQ8 = false>
 __global__ __launch_bounds__(kThreads) void matvec_kernel(
     const uint8_t* __restrict__ W, int64_t off1, int64_t off2, int64_t off3,
     const void* __restrict__ xv, float* __restrict__ y, int N, int K, int nb,
@@ -104,10 +107,109 @@ __global__ __launch_bounds__(kThreads) void matvec_kernel(
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
 
+  [[maybe_unused]] const int64_t xrec = (K + K / 8 + 15) / 16 * 16;  // bytes per Q8X vector
   auto units = [&](const uint8_t* __restrict__ W, float (&acc)[R][B]) {
-  #pragma unroll 2
+#pragma unroll 2
     for (int u = l; u < U; u += LPR) {
-      if constexpr (FMT == QMV_Q8_0 || FMT == QMV_I8_ROW) {
+      if constexpr (XQ8) {
+        constexpr bool I8 = FMT == QMV_Q8_0 || FMT == QMV_I8_ROW;
+        uint4 q[R][2];
+        float sA[R], mA[R], sB[R];
+        uint2 qh6[R];
+        uint32_t qh5[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int64_t rw = row[r];
+          if constexpr (I8) {
+            const uint4* p = reinterpret_cast<const uint4*>(W + rw * K) + 2 * u;
+            q[r][0] = p[0];
+            q[r][1] = p[1];
+            sA[r] = FMT == QMV_Q8_0 ? f16_bits_to_f32(reinterpret_cast<const uint16_t*>(W + off1)[rw * (K >> 5) + u])
+                                    : reinterpret_cast<const float*>(W + off1)[rw];
+          } else {
+            q[r][0] = reinterpret_cast<const uint4*>(W + rw * (K >> 1))[u];
+            if constexpr (FMT == QMV_Q5_0 || FMT == QMV_Q5K)
+              qh5[r] = reinterpret_cast<const uint32_t*>(W + off1)[rw * (K >> 5) + u];
+            if constexpr (FMT == QMV_W4A16_G64) {
+              const uint32_t sz = reinterpret_cast<const uint32_t*>(W + off1)[rw * (K >> 6) + (u >> 1)];
+              sA[r] = f16_bits_to_f32(sz & 0xFFFFu);
+              mA[r] = f16_bits_to_f32(sz >> 16);
+            } else if constexpr (FMT == QMV_Q4_0 || FMT == QMV_Q5_0) {
+              const int64_t dpl = FMT == QMV_Q4_0 ? off1 : off2;
+              sA[r] = f16_bits_to_f32(reinterpret_cast<const uint16_t*>(W + dpl)[rw * (K >> 5) + u]);
+            } else if constexpr (FMT == QMV_Q4K || FMT == QMV_Q5K) {
+              const uint4 rec = reinterpret_cast<const uint4*>(W + (FMT == QMV_Q4K ? off1 : off2))[rw * (K >> 8) + (u >> 3)];
+              const int j = u & 7;
+              const uint64_t lo = uint64_t(rec.y) | (uint64_t(rec.z) << 32);
+              const uint64_t hi = uint64_t(rec.z >> 16) | (uint64_t(rec.w) << 16);
+              sA[r] = f16_bits_to_f32(rec.x & 0xFFFFu) * static_cast<float>(static_cast<uint32_t>(lo >> (6 * j)) & 63u);
+              mA[r] = f16_bits_to_f32(rec.x >> 16) * static_cast<float>(static_cast<uint32_t>(hi >> (6 * j)) & 63u);
+            } else if constexpr (FMT == QMV_Q6K) {
+              qh6[r] = reinterpret_cast<const uint2*>(W + off1)[rw * (K >> 5) + u];
+              const uint32_t s2 = reinterpret_cast<const uint16_t*>(W + off2)[rw * (K >> 5) + u];
+              const float d = f16_bits_to_f32(reinterpret_cast<const uint16_t*>(W + off3)[rw * (K >> 8) + (u >> 3)]);
+              sA[r] = d * static_cast<float>(static_cast<int8_t>(s2 & 0xFFu));
+              sB[r] = d * static_cast<float>(static_cast<int8_t>(s2 >> 8));
+            }
+          }
+        }
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          const int bb = min(b, nb - 1);
+          const uint8_t* xr = static_cast<const uint8_t*>(xv) + int64_t(bb) * xrec;
+          const uint4 x0 = reinterpret_cast<const uint4*>(xr)[2 * u], x1 = reinterpret_cast<const uint4*>(xr)[2 * u + 1];
+          const float dx = reinterpret_cast<const float*>(xr + K)[u];
+          const int xw[8] = {int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
+          int sxA = 0, sxB = 0;  // code sums (Q6K: the two 16-weight halves)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            if (FMT == QMV_Q6K && j >= 4) sxB = __builtin_amdgcn_sdot4(xw[j], 0x01010101, sxB, false);
+            else sxA = __builtin_amdgcn_sdot4(xw[j], 0x01010101, sxA, false);
+          }
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            if constexpr (I8) {
+              const int ww[8] = {int(q[r][0].x), int(q[r][0].y), int(q[r][0].z), int(q[r][0].w),
+                                 int(q[r][1].x), int(q[r][1].y), int(q[r][1].z), int(q[r][1].w)};
+              int dot = 0;
+#pragma unroll
+              for (int j = 0; j < 8; ++j) dot = __builtin_amdgcn_sdot4(ww[j], xw[j], dot, false);
+              acc[r][b] = fmaf(sA[r] * dx, static_cast<float>(dot), acc[r][b]);
+            } else {
+              int dA = 0, dB = 0;
+              const uint32_t wq[4] = {q[r][0].x, q[r][0].y, q[r][0].z, q[r][0].w};
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                uint32_t ev = wq[i] & 0x0F0F0F0Fu, od = (wq[i] >> 4) & 0x0F0F0F0Fu;
+                if constexpr (FMT == QMV_Q6K) {
+                  const uint32_t h = (i >> 1) ? qh6[r].y : qh6[r].x;
+                  const int f = (i & 1) * 2;
+                  ev |= ((h >> (2 * f)) & 0x03030303u) << 4;
+                  od |= ((h >> (2 * f + 2)) & 0x03030303u) << 4;
+                } else if constexpr (FMT == QMV_Q5_0 || FMT == QMV_Q5K) {
+                  ev |= ((qh5[r] >> (2 * i)) & 0x01010101u) << 4;
+                  od |= ((qh5[r] >> (2 * i + 1)) & 0x01010101u) << 4;
+                }
+                // activation codes in the same even / odd split of k = 8i .. 8i + 7
+                const int xe = int(__builtin_amdgcn_perm(uint32_t(xw[2 * i + 1]), uint32_t(xw[2 * i]), 0x06040200u));
+                const int xo = int(__builtin_amdgcn_perm(uint32_t(xw[2 * i + 1]), uint32_t(xw[2 * i]), 0x07050301u));
+                int& d = (FMT == QMV_Q6K && i >= 2) ? dB : dA;
+                d = __builtin_amdgcn_sdot4(int(ev), xe, d, false);
+                d = __builtin_amdgcn_sdot4(int(od), xo, d, false);
+              }
+              float c;
+              if constexpr (FMT == QMV_W4A16_G64) c = sA[r] * fmaf(-mA[r], static_cast<float>(sxA), static_cast<float>(dA));
+              else if constexpr (FMT == QMV_Q4_0) c = sA[r] * static_cast<float>(dA - 8 * sxA);
+              else if constexpr (FMT == QMV_Q5_0) c = sA[r] * static_cast<float>(dA - 16 * sxA);
+              else if constexpr (FMT == QMV_Q4K || FMT == QMV_Q5K)
+                c = fmaf(sA[r], static_cast<float>(dA), -mA[r] * static_cast<float>(sxA));
+              else c = fmaf(sA[r], static_cast<float>(dA - 32 * sxA), sB[r] * static_cast<float>(dB - 32 * sxB));
+              acc[r][b] = fmaf(dx, c, acc[r][b]);
+            }
+          }
+        }
+      } else if constexpr (FMT == QMV_Q8_0 || FMT == QMV_I8_ROW) {
+
         uint4 q[R][2];
         float s[R];
   #pragma unroll
@@ -371,45 +473,45 @@ struct EpiArgs {
   const float* res;
 };
 
-template <int FMT, bool XF16, int LPR, int B, int R>
+template <int FMT, bool XF16, int LPR, int B, int R, bool XQ8>
 hipError_t go(const uint8_t* W, const Planes& p, const void* x, float* y, int N, int K, int nb,
               const EpiArgs& e, hipStream_t s) {
   constexpr int rows_per_wave = R * (64 / LPR);
   const int waves = (N + rows_per_wave - 1) / rows_per_wave;
   const int blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
   if (e.W2)
-    hipLaunchKernelGGL((matvec_kernel<FMT, XF16, LPR, B, R, true>), dim3(blocks), dim3(kThreads), 0, s, W,
+    hipLaunchKernelGGL((matvec_kernel<FMT, XF16, LPR, B, R, true, XQ8>), dim3(blocks), dim3(kThreads), 0, s, W,
                        p.off[1], p.off[2], p.off[3], x, y, N, K, nb, e.W2, nullptr, nullptr);
   else
-    hipLaunchKernelGGL((matvec_kernel<FMT, XF16, LPR, B, R>), dim3(blocks), dim3(kThreads), 0, s, W,
+    hipLaunchKernelGGL((matvec_kernel<FMT, XF16, LPR, B, R, false, XQ8>), dim3(blocks), dim3(kThreads), 0, s, W,
                        p.off[1], p.off[2], p.off[3], x, y, N, K, nb, nullptr, e.bias, e.res);
   return hipGetLastError();
 }
 
-template <int FMT, bool XF16, int LPR>
+template <int FMT, bool XF16, int LPR, bool XQ8>
 hipError_t pick_br(const uint8_t* W, const Planes& p, const void* x, float* y, int N, int K,
                    int nb, const EpiArgs& e, hipStream_t s) {
   // Two rows per lane group once there are enough rows to keep ~8 waves per CU.
   const bool two = (int64_t(N) * LPR) / 64 >= 8 * 256 * 2;
-  if (nb <= 1) return two ? go<FMT, XF16, LPR, 1, 2>(W, p, x, y, N, K, nb, e, s)
-                          : go<FMT, XF16, LPR, 1, 1>(W, p, x, y, N, K, nb, e, s);
-  if (nb <= 2) return two ? go<FMT, XF16, LPR, 2, 2>(W, p, x, y, N, K, nb, e, s)
-                          : go<FMT, XF16, LPR, 2, 1>(W, p, x, y, N, K, nb, e, s);
-  if (nb <= 4) return two ? go<FMT, XF16, LPR, 4, 2>(W, p, x, y, N, K, nb, e, s)
-                          : go<FMT, XF16, LPR, 4, 1>(W, p, x, y, N, K, nb, e, s);
-  return go<FMT, XF16, LPR, 8, 1>(W, p, x, y, N, K, nb, e, s);
+  if (nb <= 1) return two ? go<FMT, XF16, LPR, 1, 2, XQ8>(W, p, x, y, N, K, nb, e, s)
+                          : go<FMT, XF16, LPR, 1, 1, XQ8>(W, p, x, y, N, K, nb, e, s);
+  if (nb <= 2) return two ? go<FMT, XF16, LPR, 2, 2, XQ8>(W, p, x, y, N, K, nb, e, s)
+                          : go<FMT, XF16, LPR, 2, 1, XQ8>(W, p, x, y, N, K, nb, e, s);
+  if (nb <= 4) return two ? go<FMT, XF16, LPR, 4, 2, XQ8>(W, p, x, y, N, K, nb, e, s)
+                          : go<FMT, XF16, LPR, 4, 1, XQ8>(W, p, x, y, N, K, nb, e, s);
+  return go<FMT, XF16, LPR, 8, 1, XQ8>(W, p, x, y, N, K, nb, e, s);
 }
 
-template <int FMT, bool XF16>
+template <int FMT, bool XF16, bool XQ8 = false>
 hipError_t pick_lpr(const uint8_t* W, const Planes& p, const void* x, float* y, int N, int K,
                     int nb, const EpiArgs& e, hipStream_t s) {
   // Lanes per row: a whole wave per row once a row has >= 64 units (a ragged
   // last pass costs less than the parallelism lost by packing more rows into
   // a wave); shorter rows share the wave so every lane still has a unit.
   const int U = K / 32;
-  if (U >= 64) return pick_br<FMT, XF16, 64>(W, p, x, y, N, K, nb, e, s);
-  if (U > 16) return pick_br<FMT, XF16, 32>(W, p, x, y, N, K, nb, e, s);
-  return pick_br<FMT, XF16, 16>(W, p, x, y, N, K, nb, e, s);
+  if (U >= 64) return pick_br<FMT, XF16, 64, XQ8>(W, p, x, y, N, K, nb, e, s);
+  if (U > 16) return pick_br<FMT, XF16, 32, XQ8>(W, p, x, y, N, K, nb, e, s);
+  return pick_br<FMT, XF16, 16, XQ8>(W, p, x, y, N, K, nb, e, s);
 }
 
 }  // namespace
@@ -439,7 +541,8 @@ hipError_t launch_matvec_epi(int fmt, int64_t N, int64_t K, int64_t batch, const
                              hipStream_t s) {
   const Planes p = planes_of(fmt, N, K);
   const bool f16 = (x_dtype == QMV_F16);
-  const size_t xel = f16 ? 2 : 4;
+  const bool q8 = (x_dtype == QMV_Q8X);
+  const int64_t xstride = q8 ? q8x_record_bytes(K) : K * (f16 ? 2 : 4);  // bytes per vector
   const bool plain = !W2 && !bias && !res;
   if (batch == 1) {
     hipError_t e = hipSuccess;
@@ -448,11 +551,26 @@ hipError_t launch_matvec_epi(int fmt, int64_t N, int64_t K, int64_t batch, const
   }
   for (int64_t b0 = 0; b0 < batch; b0 += 8) {
     const int nb = static_cast<int>(batch - b0 < 8 ? batch - b0 : 8);
-    const void* xb = static_cast<const uint8_t*>(x) + b0 * K * xel;
+    const void* xb = static_cast<const uint8_t*>(x) + b0 * xstride;
     float* yb = y + b0 * N;
     const EpiArgs ea{W2, bias, res ? res + b0 * N : nullptr};
     hipError_t e = hipSuccess;
     if (plain && nb >= 2 && use_mfma() && launch_matvec_mfma(fmt, N, K, nb, W, xb, x_dtype, yb, s, &e)) {
+      if (e != hipSuccess) return e;
+      continue;
+    }
+    if (q8) {
+      switch (fmt) {
+        case QMV_Q8_0: e = pick_lpr<QMV_Q8_0, false, true>(W, p, xb, yb, int(N), int(K), nb, ea, s); break;
+        case QMV_W4A16_G64: e = pick_lpr<QMV_W4A16_G64, false, true>(W, p, xb, yb, int(N), int(K), nb, ea, s); break;
+        case QMV_Q4K: e = pick_lpr<QMV_Q4K, false, true>(W, p, xb, yb, int(N), int(K), nb, ea, s); break;
+        case QMV_Q6K: e = pick_lpr<QMV_Q6K, false, true>(W, p, xb, yb, int(N), int(K), nb, ea, s); break;
+        case QMV_Q4_0: e = pick_lpr<QMV_Q4_0, false, true>(W, p, xb, yb, int(N), int(K), nb, ea, s); break;
+        case QMV_Q5_0: e = pick_lpr<QMV_Q5_0, false, true>(W, p, xb, yb, int(N), int(K), nb, ea, s); break;
+        case QMV_Q5K: e = pick_lpr<QMV_Q5K, false, true>(W, p, xb, yb, int(N), int(K), nb, ea, s); break;
+        case QMV_I8_ROW: e = pick_lpr<QMV_I8_ROW, false, true>(W, p, xb, yb, int(N), int(K), nb, ea, s); break;
+        default: return hipErrorInvalidValue;
+      }
       if (e != hipSuccess) return e;
       continue;
     }

@@ -643,6 +643,7 @@ bool pick_kf(MTable& t, hipStream_t s, hipError_t* err) {
 }
 
 bool launch_table(int fmt, MTable& t, int x_dtype, hipStream_t s, hipError_t* err) {
+  if (x_dtype == QMV_Q8X) return false;  // 8-bit activations run on the general kernel
   const bool f16 = (x_dtype == QMV_F16);
   switch (fmt) {
     case QMV_Q8_0: return pick_kf<QMV_Q8_0, false>(t, s, err);
@@ -689,6 +690,7 @@ bool launch_matvec_mfma(int fmt, int64_t N, int64_t K, int nv, const uint8_t* W,
 // kernel's range.
 bool launch_matvec_grouped_mfma(int fmt, int64_t K, int64_t batch, int count, const qmv_matvec_item* items,
                                 int x_dtype, hipStream_t s, hipError_t* err) {
+  if (x_dtype == QMV_Q8X) return false;  // 8-bit activations run on the general kernel
   auto eff = [&](int i) { return items[i].fmt ? items[i].fmt : fmt; };
   for (int i = 0; i < count; ++i)  // decided before anything is launched
     if (!has_kernel(eff(i)) || !fits(eff(i), items[i].N, K)) return false;

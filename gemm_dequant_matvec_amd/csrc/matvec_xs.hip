@@ -904,6 +904,7 @@ int rows_override() {
 }
 
 bool launch_table(int fmt, SegTable& t, int x_dtype, hipStream_t s, hipError_t* err) {
+  if (x_dtype == QMV_Q8X) return false;  // 8-bit activations run on the general kernel
   const int rsel = rows_override();
   const bool f16 = (x_dtype == QMV_F16);
   switch (fmt) {
@@ -972,6 +973,7 @@ bool launch_matvec_b1_epi(int fmt, int64_t N, int64_t K, const uint8_t* W, const
 // kernels.
 bool launch_matvec_grouped_b1(int fmt, int64_t K, int count, const qmv_matvec_item* items, int x_dtype,
                               hipStream_t s, hipError_t* err) {
+  if (x_dtype == QMV_Q8X) return false;  // 8-bit activations run on the general kernel
   const int U = int(K) / 32;
   const int lpr = U >= 64 ? 64 : (U > 16 ? 32 : 16);
   const int upl = (U + lpr - 1) / lpr;

@@ -143,6 +143,8 @@ bool launch_matvec_grouped_mfma(int fmt, int64_t K, int64_t batch, int count, co
                                 int x_dtype, hipStream_t s, hipError_t* err);
 bool launch_matvec_grouped_b1(int fmt, int64_t K, int count, const qmv_matvec_item* items, int x_dtype,
                               hipStream_t s, hipError_t* err);
+int64_t q8x_record_bytes(int64_t K);  // bytes per vector of a QMV_Q8X buffer
+hipError_t launch_quantize_x(int64_t K, int64_t batch, const float* x, uint8_t* xq, hipStream_t s);
 hipError_t launch_gemm(int fmt, int64_t N, int64_t K, int64_t M, const uint8_t* W,
                        const uint16_t* X, uint16_t* Y, hipStream_t s);
 

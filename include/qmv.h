@@ -129,7 +129,8 @@ enum qmv_format {
 enum qmv_dtype {
   QMV_F32 = 1,
   QMV_F16 = 2,
-  QMV_BF16 = 3
+  QMV_BF16 = 3,
+  QMV_Q8X = 4  /* activations quantized to 8-bit blocks by qmv_quantize_x (layout below) */
 };
 
 enum qmv_status {
@@ -294,6 +295,36 @@ int qmv_matvec_grouped(int fmt, int64_t K, int64_t batch, int count, const qmv_m
  */
 int qmv_gemm(int fmt, int64_t N, int64_t K, int64_t M, const void* W, const void* X,
              int x_dtype, void* Y, int y_dtype, void* stream);
+
+/*
+ * Quantize `batch` f32 activation vectors x [batch][K] (K a multiple of 32) to
+ * 8-bit blocks, once, for the integer-dot matvec: per vector and block of 32,
+ *   amax = max |x_k|,  d = amax / 127,  id = 127 / amax,
+ *   q_k = rint(x_k * id) clamped to [-127, 127]   (f32 operations, round to
+ *   nearest even; the quantized activation is d * q_k),
+ * except that a block with amax < 2^-120 (where 127 / amax could overflow)
+ * gets d = 0 and zero codes.  x must be finite (otherwise the codes are
+ * unspecified)
+ * (aot-llm README, How it works: per matmul the f32 activation vector is
+ * quantized once to 8-bit blocks and every output row is an integer dot
+ * product scaled back to f32).  xq receives, per vector b at byte
+ * b * R with R = (K + K/8) rounded up to 16: K int8 codes, then K/32 f32
+ * scales d; qmv_q8x_bytes gives the size.  Codes and scales are unique bit
+ * for bit.  Pass xq to qmv_matvec / qmv_matvec_ex / qmv_matvec_swiglu /
+ * qmv_matvec_grouped with x_dtype QMV_Q8X: the formats Q8_0, W4A16_G64, Q4K,
+ * Q6K, Q4_0, Q5_0, Q5K and I8_ROW then take integer dot products (exact in
+ * int32) per 32-weight block, scaled back in f32.  The result matches the
+ * product over d * q within the matvec tolerance; against the f32 x it also
+ * carries the quantization error (|x - d q| <= d / 2 per element, about
+ * 5e-3 relative for N(0,1) activations).
+ * Errors: SHAPE (K not a multiple of 32, batch < 1), NULL, ALIGN (16 bytes),
+ * OVERFLOW, DEVICE, LAUNCH.
+ */
+int qmv_quantize_x(int64_t K, int64_t batch, const float* x, void* xq, void* stream);
+
+/* Bytes of the qmv_quantize_x output for `batch` vectors of K.  Host only.
+ * Errors: SHAPE, NULL, OVERFLOW. */
+int qmv_q8x_bytes(int64_t K, int64_t batch, size_t* out_bytes);
 
 /*
  * Dense f32 dequantization of one packed matrix into out [N][K] (device),

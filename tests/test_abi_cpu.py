@@ -24,14 +24,14 @@ def q():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(qmv_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(qmv_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
         ["qmv_abi_version", "qmv_status_string", "qmv_last_error", "qmv_packed_bytes",
          "qmv_pack", "qmv_matvec", "qmv_matvec_ex", "qmv_matvec_swiglu", "qmv_matvec_grouped", "qmv_gemm",
-         "qmv_dequant"])
+         "qmv_dequant", "qmv_quantize_x", "qmv_q8x_bytes"])
 
 
 def test_library_exports_every_declared_symbol(q):
@@ -170,3 +170,18 @@ def test_epilogue_and_swiglu_argument_errors(q):
     assert sw(3, 64, 256, 1, P, P + 8, P, 1, P, 1, None) == -5
     assert "W_up" in q.last_error()
     assert sw(3, 64, 256, 1, P, P, P, 2, P, 1, None) == -3      # f16 x for Q4K
+
+
+def test_q8x_sizes_and_errors(q):
+    for K, b in ((32, 1), (96, 3), (2048, 8), (5632, 11)):
+        assert q.q8x_bytes(K, b) == b * oracle.q8x_record_bytes(K)
+    out = ctypes.c_size_t(0)
+    assert q.raw_call("qmv_q8x_bytes", 48, 1, ctypes.byref(out)) == -4
+    assert q.raw_call("qmv_q8x_bytes", 64, 0, ctypes.byref(out)) == -4
+    assert q.raw_call("qmv_q8x_bytes", 64, 1, None) == -1
+    P = 1 << 20
+    assert q.raw_call("qmv_quantize_x", 64, 1, None, P, None) == -1
+    assert q.raw_call("qmv_quantize_x", 64, 1, P, P + 4, None) == -5
+    # Q8X activations: any integer-code format, not dense bf16
+    assert q.raw_call("qmv_matvec", 8, 64, 256, 1, P, P, 4, P, 1, None) == -3
+    assert "DENSE_BF16" in q.last_error()
