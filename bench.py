@@ -18,12 +18,15 @@ streamed bandwidth), GB/s = bytes / time.
 
 Also reported (`extras`): single-launch and cold-stream rates of the other
 workloads (Q8_0 512x512, Q4K 0.6B MLP and 151936-row vocab head, the full
-155-matvec 1.1B decode sweep at batch 1 and 8, the W4A16 prefill GEMM at
-M = 16 / 128 / 512 in TFLOP/s), a plain-copy bandwidth probe, and the CPU
-oracle timed on the host (`cpu_baseline`).
+155-matvec 1.1B decode sweep at batch 1 and 8 -- grouped, with the fused
+epilogues, and with 8-bit activation blocks -- the W4A16 prefill GEMM at
+M = 16 / 128 / 512 in TFLOP/s), each with its fraction of peak and
+tokens-equivalent rate (`gated` collects the roofline-gated ones), platform
+probes, and the CPU oracle timed on the host (`cpu_baseline`: per config,
+median of 3, dequantization and product split, and one BLAS thread).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--copies C]
-                       [--no-extras] [--no-cpu-baseline] [--leg NAME]
+                       [--no-extras] [--no-cpu-baseline] [--cpu-quick] [--leg NAME]
 (--leg runs one extras workload alone and prints its result, for profiling.)
 """
 from __future__ import annotations
@@ -39,6 +42,12 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+# Tokens-equivalent per second (bytes-per-token roofline method, zynfer PR 100,
+# stage M2): a matvec figure in GB/s divided by the bytes of one decode token of
+# the 1.1B decoder (packed weights of its 155 matvecs); a GEMM figure in
+# TFLOP/s divided by 2 flops per weight of that model.
+TOKEN_BYTES_1B1 = 667_152_384
+TOKEN_FLOPS_1B1 = 2 * 1_034_420_224
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published
 
@@ -55,8 +64,8 @@ def parse():
     p.add_argument("--copies", type=int, default=32)
     p.add_argument("--no-extras", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=12.0,
-                   help="target CPU time of the oracle sample")
+    p.add_argument("--cpu-quick", action="store_true",
+                   help="skip the oracle's decode-token run (c5) in the CPU baseline")
     p.add_argument("--leg", default=None,
                    help="run only this extras workload and print its result (profiling); one of: "
                         + ", ".join(LEGS))
@@ -315,14 +324,21 @@ def platform_probes(qmv):
     return out
 
 
+def _gbs_result(d, gbs):
+    d.update({"gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+              "tok_per_s_equiv": gbs * 1e9 / TOKEN_BYTES_1B1,
+              "tok_note": "GB/s / bytes of one 1.1B decode token (667152384 B)"})
+    return d
+
+
 def leg_q8_0(qmv):
     """Q8_0 512x512: one launch, latency-bound (same matrix 20x back to back)."""
     import workloads as wl
     st = Stream(qmv, wl.c1_q8_0()["mats"], "f32", 1, 1)
     ms, _ = time_graph(lambda: [st() for _ in range(20)], 20, 5)
     ms /= 20
-    return {"us": ms * 1e3, "gbs": st.bytes / (ms * 1e-3) / 1e9,
-            "note": "same matrix 20x back to back (cache-warm)"}
+    return _gbs_result({"us": ms * 1e3, "note": "same matrix 20x back to back (cache-warm, latency-bound)"},
+                       st.bytes / (ms * 1e-3) / 1e9)
 
 
 def leg_mlp06(qmv):
@@ -331,8 +347,8 @@ def leg_mlp06(qmv):
     mlp = [m for m in wl.c3_q4k_0b6()["mats"] if m[0] != "head"]
     st = Stream(qmv, mlp, "f32", 1, 170)
     ms, _ = time_graph(st, 10, 3)
-    return {"us_per_launch": ms * 1e3 / st.launches, "gbs": st.bytes / (ms * 1e-3) / 1e9,
-            "launches": st.launches}
+    return _gbs_result({"us_per_launch": ms * 1e3 / st.launches, "launches": st.launches},
+                       st.bytes / (ms * 1e-3) / 1e9)
 
 
 def leg_head06(qmv):
@@ -341,7 +357,14 @@ def leg_head06(qmv):
     head = [m for m in wl.c3_q4k_0b6()["mats"] if m[0] == "head"]
     st = Stream(qmv, head, "f32", 1, 8)
     ms, _ = time_graph(st, 10, 3)
-    return {"us_per_launch": ms * 1e3 / st.launches, "gbs": st.bytes / (ms * 1e-3) / 1e9}
+    return _gbs_result({"us_per_launch": ms * 1e3 / st.launches, "bytes_per_launch": st.bytes // st.launches},
+                       st.bytes / (ms * 1e-3) / 1e9)
+
+
+def _sweep_result(ms, b, nbytes, launches, matvecs):
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"ms_per_token_step": ms, "tok_per_s": b / (ms * 1e-3), "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+            "bytes": nbytes, "launches": launches, "matvecs": matvecs}
 
 
 def leg_sweep(qmv, b):
@@ -349,8 +372,28 @@ def leg_sweep(qmv, b):
     import workloads as wl
     st = Sweep(qmv, wl.c5_sweep(b), b)
     ms, _ = time_graph(st, 10, 3)
-    return {"ms_per_token_step": ms, "tok_per_s": b / (ms * 1e-3), "gbs": st.bytes / (ms * 1e-3) / 1e9,
-            "bytes": st.bytes, "launches": st.launches, "matvecs": st.matvecs}
+    return _sweep_result(ms, b, st.bytes, st.launches, st.matvecs)
+
+
+def leg_sweep_q8x(qmv, b):
+    """The same token with the integer-dot variant: each distinct activation
+    vector quantized once per step (included in the time), integer dot products."""
+    import workloads as wl
+    st = Sweep(qmv, wl.c5_sweep(b), b)
+    step = st.with_q8x()
+    ms, _ = time_graph(step, 10, 3)
+    r = _sweep_result(ms, b, step.bytes, step.launches, st.matvecs)
+    r["note"] = "bytes as the f32 sweep; launches include one quantize per distinct x"
+    return r
+
+
+def leg_sweep_fused(qmv, b):
+    """The token with fused epilogues: o and down add the residual in place,
+    gate / up / SwiGLU in one pass (h written once)."""
+    import workloads as wl
+    st = FusedSweep(qmv, wl.c5_sweep(b), b)
+    ms, _ = time_graph(st, 10, 3)
+    return _sweep_result(ms, b, st.bytes, st.launches, st.matvecs)
 
 
 LEGS = {
@@ -360,6 +403,10 @@ LEGS = {
     "q4k_vocab_head_151936x1024_b1_cold": leg_head06,
     "decode_sweep_1.1B_b1": lambda q: leg_sweep(q, 1),
     "decode_sweep_1.1B_b8": lambda q: leg_sweep(q, 8),
+    "decode_sweep_1.1B_b1_fused": lambda q: leg_sweep_fused(q, 1),
+    "decode_sweep_1.1B_b8_fused": lambda q: leg_sweep_fused(q, 8),
+    "decode_sweep_1.1B_b1_q8x": lambda q: leg_sweep_q8x(q, 1),
+    "decode_sweep_1.1B_b8_q8x": lambda q: leg_sweep_q8x(q, 8),
     "gemm_w4a16_M16": lambda q: gemm_leg(q, 16),
     "gemm_w4a16_M128": lambda q: gemm_leg(q, 128),
     "gemm_w4a16_M512": lambda q: gemm_leg(q, 512),
@@ -426,6 +473,104 @@ class Sweep:
             else:
                 self.qmv.matvec_grouped(fmt, items, K)
 
+    def with_q8x(self):
+        """The integer-dot variant of the same sweep: every distinct activation
+        vector is quantized to 8-bit blocks once (qmv_quantize_x, inside the
+        step), and each matvec reads the quantized copy."""
+        bufs, calls = {}, []
+        for fmt, K, items in self.calls:
+            new = []
+            for W, x, N, y, f in items:
+                if id(x) not in bufs:
+                    bufs[id(x)] = (x, self.qmv.quantize_x(x))
+                new.append((W, bufs[id(x)][1], N, y, f))
+            calls.append((fmt, K, new))
+        pairs = list(bufs.values())
+        qmv = self.qmv
+        # quantize each distinct vector right before its first use
+        first_use = {}
+        for ci, (fmt, K, items) in enumerate(calls):
+            for W, xq, N, y, f in items:
+                first_use.setdefault(id(xq), ci)
+        quant_at = {}
+        for x, xq in pairs:
+            quant_at.setdefault(first_use[id(xq)], []).append((x, xq))
+
+        def step():
+            for ci, (fmt, K, items) in enumerate(calls):
+                for x, xq in quant_at.get(ci, ()):
+                    qmv.quantize_x(x, out=xq.data)
+                if len(items) == 1:
+                    W, xq, N, y, _ = items[0]
+                    qmv.matvec(fmt, W, xq, N, K, y=y)
+                else:
+                    qmv.matvec_grouped(fmt, items, K)
+        step.launches = len(calls) + len(pairs)
+        step.bytes = self.bytes  # the same algorithmic bytes as the f32 sweep
+        return step
+
+
+class FusedSweep:
+    """One decode token of the 1.1B decoder with the fused epilogues: per layer
+    q + k + v grouped; o with the residual add fused (the residual stream is
+    updated in place); gate / up / SwiGLU in one pass writing h; down reading h
+    with the residual add fused; then the vocab head.  Four launches per layer
+    plus the head, as in the grouped sweep, but the MLP writes one vector
+    instead of two and no separate add runs.  Every layer has its own device
+    copy of the weights (distinct shapes generated once, then cloned)."""
+
+    def __init__(self, qmv, cfg, batch):
+        import torch
+        import workloads as wl
+        self.qmv, self.batch = qmv, batch
+        packed, shapes = {}, {}
+        for name, fmt, N, K, key in cfg["mats"]:
+            tag = (fmt, N, K)
+            if tag not in shapes:
+                w = wl.gen_weights(fmt, N, K, key)
+                shapes[tag] = qmv.pack(fmt, {k: _dev(v) for k, v in w.items()})
+                packed[name] = shapes[tag]
+            else:
+                packed[name] = shapes[tag].clone()
+        f32 = dict(dtype=torch.float32, device="cuda")
+        D, F = wl.LLAMA_1B1["dim"], wl.LLAMA_1B1["mlp"]
+        gx = lambda K, k: _x_dev(wl.gen_x(K, batch, "f32", (5, 2000, k)), "f32")
+        self.resid = gx(D, 0)
+        self.layers = []
+        nbytes = 0
+        n_layers = sum(1 for m in cfg["mats"] if m[0].endswith(".q"))
+        for L in range(n_layers):
+            W = {nm: packed[f"l{L}.{nm}"] for nm in ("q", "k", "v", "o", "gate", "up", "down")}
+            lay = dict(W=W, attn_in=gx(D, 10 * L + 1), o_in=gx(D, 10 * L + 2), mlp_in=gx(D, 10 * L + 3),
+                       q=torch.empty((batch, D), **f32), k=torch.empty((batch, 256), **f32),
+                       v=torch.empty((batch, 256), **f32), h=torch.empty((batch, F), **f32))
+            self.layers.append(lay)
+        for name, fmt, N, K, key in cfg["mats"]:
+            nbytes += int(round(wl.bytes_per_weight(fmt) * N * K))
+        V = wl.LLAMA_1B1["vocab"]
+        self.head = (packed["head"], gx(D, 9999), torch.empty((batch, V), **f32), V)
+        xb, L = batch * 4, n_layers
+        # activations: per layer attn_in, o_in, mlp_in, h read; q, k, v, h written;
+        # residual read + written twice; head x in, logits out
+        nbytes += L * xb * (3 * D + F + (D + 256 + 256 + F) + 4 * D) + xb * (D + V)
+        self.bytes = nbytes
+        self.launches = 4 * L + 1
+        self.matvecs = 7 * L + 1
+
+    def __call__(self):
+        qmv, r = self.qmv, self.resid
+        D, F = r.shape[1], self.layers[0]["h"].shape[1]
+        for lay in self.layers:
+            W = lay["W"]
+            qmv.matvec_grouped(None, [(W["q"], lay["attn_in"], D, lay["q"], "q4k"),
+                                      (W["k"], lay["attn_in"], 256, lay["k"], "q4k"),
+                                      (W["v"], lay["attn_in"], 256, lay["v"], "q6k")], D)
+            qmv.matvec_ex("q4k", W["o"], lay["o_in"], D, D, y=r, residual=r)
+            qmv.matvec_swiglu("q4k", W["gate"], W["up"], lay["mlp_in"], F, D, h=lay["h"])
+            qmv.matvec_ex("q6k", W["down"], lay["h"], D, F, y=r, residual=r)
+        Wh, xh, yh, V = self.head
+        qmv.matvec("q6k", Wh, xh, V, D, y=yh)
+
 
 def gemm_leg(qmv, M, reps=20):
     """Prefill GEMM time per launch: a graph of `reps` back-to-back launches, so the
@@ -468,37 +613,141 @@ def gemm_leg(qmv, M, reps=20):
     ms_bl /= reps
     del WdT
     return {"us": ms * 1e3, "tflops": tf, "frac_bf16_peak": tf / BF16_PEAK_TFLOPS,
+            "tok_per_s": M / (ms * 1e-3), "prefill_tok_per_s_equiv": tf * 1e12 / TOKEN_FLOPS_1B1,
             "matvec_path_us": ms_mv * 1e3, "dense_bf16_library_gemm_us": ms_bl * 1e3,
             "dense_bf16_library_frac_peak": flops / (ms_bl * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
 
 
-def cpu_baseline(st, seconds):
-    """The oracle, untuned, on the host: f32 dequantization + f64 product of the
-    headline matrices (copy 0), repeated until about `seconds` of CPU work."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_matvecs(oracle, mats, reps=1):
+    """Dequantize + f64 product of each (fmt, w, x) `reps` times; (dequant s, product s)."""
+    import numpy as np
+    t_dq = t_mv = 0.0
+    for _ in range(reps):
+        for fmt, w, x, xdt in mats:
+            t0 = time.perf_counter()
+            W = oracle.dequant(fmt, w)
+            t1 = time.perf_counter()
+            xv = oracle.f16_to_f64(x) if xdt == "f16" else x.astype(np.float64)
+            oracle.matvec_ref(W, xv)
+            t_mv += time.perf_counter() - t1
+            t_dq += t1 - t0
+            del W
+    return t_dq, t_mv
+
+
+def cpu_baseline(args):
+    """The oracle, untuned, on the host: numpy f32 dequantization (one thread)
+    and the f64 product (BLAS, as many threads as cores this process may use).
+    Per config the median of 3 runs (1 for the decode token), split into
+    dequantization and product time; c1-c3 also with one BLAS thread.  Inputs
+    are generated before timing.  `value` is the headline workload's rate."""
+    import statistics
     import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        blas = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    except Exception:
-        blas = 1
-    done_bytes, t0, passes = 0, time.perf_counter(), 0
-    while True:
-        for name in st.logical:
-            fmt, w, x = st.logical[name]
+    import workloads as wl
+    from threadpoolctl import threadpool_limits
+    cores = len(os.sched_getaffinity(0))
+
+    def mats_of(cfg):
+        xdt = cfg["x_dtype"]
+        return [(fmt, wl.gen_weights(fmt, N, K, key), wl.gen_x(K, cfg["batch"], xdt, key), xdt)
+                for _, fmt, N, K, key in cfg["mats"]]
+
+    def cfg_bytes(cfg):
+        xb = {"f32": 4, "f16": 2, "bf16": 2}[cfg["x_dtype"]]
+        return sum(matvec_bytes(fmt, N, K, cfg["batch"], xb) for _, fmt, N, K, _ in cfg["mats"])
+
+    def timed(mats, nbytes, runs):
+        res = [_oracle_matvecs(oracle, mats) for _ in range(runs)]
+        tot = [a + b for a, b in res]
+        med = statistics.median(tot)
+        k = tot.index(med) if med in tot else 0
+        return {"s": med, "dequant_s": res[k][0], "product_s": res[k][1], "runs": runs,
+                "gbs": nbytes / med / 1e9}
+
+    per = {}
+    t_start = time.perf_counter()
+    cfgs = {"c1_q8_0_512x512_b1": wl.c1_q8_0(), "c2_w4a16_1.1B_mlp_b1": wl.c2_w4a16_mlp(),
+            "c3_q4k_0.6B_mlp_head_b1": wl.c3_q4k_0b6()}
+    with threadpool_limits(limits=cores):
+        for tag, cfg in cfgs.items():
+            per[tag] = timed(mats_of(cfg), cfg_bytes(cfg), 3)
+        # c4: the GEMM at M = 512 (dequantize + f64 X W^T)
+        _, fmt, N, K, key = wl.c4_gemm(512)["mats"][0]
+        w, X = wl.gen_weights(fmt, N, K, key), oracle.bf16_to_f64(wl.gen_x(K, 512, "bf16", key))
+        runs = []
+        for _ in range(3):
+            t0 = time.perf_counter()
             W = oracle.dequant(fmt, w)
-            xv = oracle.f16_to_f64(x) if st.x_dtype == "f16" else x.astype(np.float64)
-            oracle.matvec_ref(W, xv)
-            N, K = w["q"].shape
-            done_bytes += matvec_bytes(fmt, N, K, 1, 2)
-        passes += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": done_bytes / dt / 1e9, "unit": "GB/s", "cores": blas, "kind": "oracle",
-            "sample": f"{passes} pass(es) over gate+up+down (one 1.1B MLP layer, W4A16 g64, b=1): "
-                      f"numpy f32 dequant (1 thread) + f64 matvec (BLAS, {blas} threads), "
-                      f"{dt:.1f} s"}
+            t1 = time.perf_counter()
+            oracle.gemm_ref(W, X)
+            runs.append((t1 - t0, time.perf_counter() - t1))
+        tot = sorted(runs, key=lambda r: r[0] + r[1])[1]
+        per["c4_w4a16_gemm_M512"] = {"s": tot[0] + tot[1], "dequant_s": tot[0], "product_s": tot[1], "runs": 3,
+                                     "tflops": 2.0 * 512 * N * K / (tot[0] + tot[1]) / 1e12}
+        if not args.cpu_quick:
+            # c5: one decode token at batch 1 (distinct shapes generated once, each run as many
+            # times as the token has such matrices; the oracle's time does not depend on values)
+            cfg = wl.c5_sweep(1)
+            counts, first = {}, {}
+            for name, fmt, N, K, key in cfg["mats"]:
+                counts[(fmt, N, K)] = counts.get((fmt, N, K), 0) + 1
+                first.setdefault((fmt, N, K), key)
+            t_dq = t_mv = 0.0
+            for (fmt, N, K), key in first.items():
+                m = [(fmt, wl.gen_weights(fmt, N, K, key), wl.gen_x(K, 1, "f32", key), "f32")]
+                a, b = _oracle_matvecs(oracle, m, reps=counts[(fmt, N, K)])
+                t_dq, t_mv = t_dq + a, t_mv + b
+            per["c5_decode_token_1.1B_b1"] = {"s": t_dq + t_mv, "dequant_s": t_dq, "product_s": t_mv, "runs": 1,
+                                              "tok_per_s": 1.0 / (t_dq + t_mv),
+                                              "gbs": cfg_bytes(cfg) / (t_dq + t_mv) / 1e9}
+    one = {}
+    with threadpool_limits(limits=1):
+        for tag, cfg in cfgs.items():
+            one[tag] = timed(mats_of(cfg), cfg_bytes(cfg), 1)
+    head = per["c2_w4a16_1.1B_mlp_b1"]
+    return {"value": head["gbs"], "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "cpu_model": _cpu_model(), "blas_threads": cores,
+            "sample": "headline workload (one 1.1B MLP layer: gate, up, down, W4A16 g64, b=1, fp16 x), "
+                      "median of 3: numpy f32 dequant (1 thread) + f64 matvec (BLAS); "
+                      f"whole baseline {time.perf_counter() - t_start:.1f} s",
+            "per_config": per, "one_blas_thread": one,
+            "note": "correctness oracle, not a tuned CPU kernel"}
+
+
+def gated_figures(out):
+    """The figures held against the roofline: the 1.1B decode token at batch 1
+    (grouped and fused), the 151936-row vocab head and the W4A16 MLP stream
+    against HBM; the W4A16 GEMM at M = 512 against bf16 MFMA; each with its
+    tokens-equivalent rate."""
+    ex = out.get("extras", {})
+    g = {"c2_w4a16_mlp_stream_b1": {"gbs": out["value"], "frac_hbm": out["value"] / HBM_PEAK_GBS,
+                                    "tok_per_s_equiv": out["value"] * 1e9 / TOKEN_BYTES_1B1}}
+    for tag, leg in (("c5_decode_token_b1", "decode_sweep_1.1B_b1"),
+                     ("c5_decode_token_b1_fused", "decode_sweep_1.1B_b1_fused"),
+                     ("c5_decode_token_b8", "decode_sweep_1.1B_b8"),
+                     ("c3_q4k_vocab_head", "q4k_vocab_head_151936x1024_b1_cold")):
+        r = ex.get(leg, {})
+        if "gbs" in r:
+            g[tag] = {"gbs": r["gbs"], "frac_hbm": r["gbs"] / HBM_PEAK_GBS,
+                      "tok_per_s" if "tok_per_s" in r else "tok_per_s_equiv":
+                          r.get("tok_per_s", r.get("tok_per_s_equiv"))}
+    r = ex.get("gemm_w4a16_M512", {})
+    if "tflops" in r:
+        g["c4_w4a16_gemm_M512"] = {"tflops": r["tflops"], "frac_bf16_mfma": r["frac_bf16_peak"],
+                                   "tok_per_s": r["tok_per_s"],
+                                   "prefill_tok_per_s_equiv": r["prefill_tok_per_s_equiv"]}
+    return g
 
 
 def main():
@@ -547,9 +796,10 @@ def main():
     if not args.no_extras:
         log("extras")
         out["extras"] = extras(qmv, args)
+        out["gated"] = gated_figures(out)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        out["cpu_baseline"] = cpu_baseline(st, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(args)
     print(json.dumps(out), flush=True)
 
 
