@@ -51,3 +51,21 @@ def check_matvec(qmv, fmt, w, x, x_dtype, rows=None, tau=None):
     ref = oracle.matvec_ref(W32, xv)
     bound = oracle.tolerance_bound(W32, xv, tau or TAU["matvec"])
     return oracle.check_within(y[:, rows], ref, bound), y, ref
+
+
+def check_every_row(fmt, w, y, xv, tau=None, chunk=8192):
+    """Compare every output row of y [b][N] with the oracle, dequantizing the
+    matrix in chunks of rows (vocab heads would not fit as one f64 block)."""
+    N = w["q"].shape[0]
+    worst = {"ok": True, "max_ratio": 0.0, "rows": N}
+    for r0 in range(0, N, chunk):
+        rows = np.arange(r0, min(N, r0 + chunk))
+        W32 = oracle.dequant_rows(fmt, w, rows)
+        r = oracle.check_within(y[:, rows], oracle.matvec_ref(W32, xv),
+                                oracle.tolerance_bound(W32, xv, tau or TAU["matvec"]))
+        worst["ok"] = worst["ok"] and r["ok"]
+        worst["max_ratio"] = max(worst["max_ratio"], r["max_ratio"])
+        if not r["ok"]:
+            worst["first_bad_chunk"] = (r0, r)
+            break
+    return worst

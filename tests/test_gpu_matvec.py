@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import workloads as wl
-from gpu_helpers import check_matvec, dev, dev_x, pack_dev, x_values
+from gpu_helpers import check_every_row, check_matvec, dev, dev_x, pack_dev, x_values
 
 pytestmark = pytest.mark.gpu
 
@@ -316,25 +316,32 @@ def test_config_w4a16_mlp(qmv):
         assert r["ok"], r
 
 
+def _run_every_row(qmv, fmt, w, x, xd):
+    N, K = w["q"].shape
+    y = qmv.matvec(fmt, pack_dev(qmv, fmt, w), dev_x(x, xd), N, K)
+    torch.cuda.synchronize()
+    return check_every_row(fmt, w, y.cpu().numpy(), x_values(x, xd))
+
+
 def test_config_q4k_mlp_and_vocab_head(qmv):
+    # every output, the 151936-row head included (oracle in row chunks)
     c = wl.c3_q4k_0b6()
     for name, fmt, N, K, key in c["mats"]:
         w = wl.gen_weights(fmt, N, K, key)
         x = wl.gen_x(K, c["batch"], c["x_dtype"], key)
-        rows = _sample_rows(N) if N > 20000 else None
-        r, _, _ = check_matvec(qmv, fmt, w, x, c["x_dtype"], rows=rows)
+        r = _run_every_row(qmv, fmt, w, x, c["x_dtype"])
         _say(name, r)
         assert r["ok"], r
 
 
 @pytest.mark.parametrize("batch", [1, 8])
 def test_config_decode_sweep_layer_and_head(qmv, batch):
+    # every output of one layer's seven matvecs and the 32000-row Q6K head
     c = wl.c5_sweep(batch, layers=1)
     for name, fmt, N, K, key in c["mats"]:
         w = wl.gen_weights(fmt, N, K, key)
         x = wl.gen_x(K, batch, "f32", key)
-        rows = _sample_rows(N) if N > 20000 else None
-        r, _, _ = check_matvec(qmv, fmt, w, x, "f32", rows=rows)
+        r = _run_every_row(qmv, fmt, w, x, "f32")
         _say(name, batch, r)
         assert r["ok"], (name, r)
 
