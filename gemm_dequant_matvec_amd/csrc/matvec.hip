@@ -455,7 +455,7 @@ __global__ __launch_bounds__(kThreads) void matvec_kernel(
       if (rr < N && b < nb) {
         float out;
         if constexpr (PAIR) {
-          out = v[0] / (1.0f + expf(-v[0])) * up;
+          out = silu_mul(v[0], up);
         } else {
           out = v[0];
           if (bias) out += bias[rr];
@@ -535,7 +535,8 @@ hipError_t launch_matvec(int fmt, int64_t N, int64_t K, int64_t batch, const uin
 
 // With a fused epilogue (W2: SwiGLU; else bias / res, null: none).  Batch 1
 // runs on the streaming kernel, 2..8 vectors per pass on the matrix-core
-// kernel when there is no epilogue, otherwise on the FMA kernel.
+// kernel for its formats (Q8_0, W4A16, Q4K, Q6K) and f32 / f16 activations,
+// otherwise on the FMA kernel.
 hipError_t launch_matvec_epi(int fmt, int64_t N, int64_t K, int64_t batch, const uint8_t* W, const uint8_t* W2,
                              const void* x, int x_dtype, float* y, const float* bias, const float* res,
                              hipStream_t s) {
@@ -555,7 +556,8 @@ hipError_t launch_matvec_epi(int fmt, int64_t N, int64_t K, int64_t batch, const
     float* yb = y + b0 * N;
     const EpiArgs ea{W2, bias, res ? res + b0 * N : nullptr};
     hipError_t e = hipSuccess;
-    if (plain && nb >= 2 && use_mfma() && launch_matvec_mfma(fmt, N, K, nb, W, xb, x_dtype, yb, s, &e)) {
+    if (nb >= 2 && use_mfma() &&
+        launch_matvec_mfma_epi(fmt, N, K, nb, W, W2, xb, x_dtype, yb, bias, ea.res, s, &e)) {
       if (e != hipSuccess) return e;
       continue;
     }

@@ -84,6 +84,20 @@ struct MTableT {
   MSeg s[CAP];
   int count, K, nv, waves;
 };
+// A single matvec with a fused epilogue (one segment): W2 != null runs
+// SwiGLU, y = silu(W x) * (W2 x), W2 of the same format and shape; otherwise
+// y = res + (W x + bias) with either pointer possibly null.
+struct MEpi {
+  const uint8_t* W2;
+  const float* bias;
+  const float* res;  // [nv][N]
+};
+struct MTableEpi {
+  int first[1];
+  MSeg s[1];
+  int count, K, nv, waves;
+  MEpi ep;
+};
 using MTable = MTableT<kMaxSeg>;  // built on the host, then shrunk to the launch
 
 template <int CAP>
@@ -97,6 +111,18 @@ MTableT<CAP> shrink(const MTable& t) {  // t.count <= CAP
   o.K = t.K;
   o.nv = t.nv;
   o.waves = t.waves;
+  return o;
+}
+
+MTableEpi with_epi(const MTable& t, const MEpi& ep) {  // t.count == 1
+  MTableEpi o{};
+  o.first[0] = t.first[0];
+  o.s[0] = t.s[0];
+  o.count = 1;
+  o.K = t.K;
+  o.nv = t.nv;
+  o.waves = t.waves;
+  o.ep = ep;
   return o;
 }
 
@@ -405,7 +431,10 @@ struct Staging {
 //
 // One workgroup's share of one segment: stage is the workgroup's staging LDS
 // (SD dwords per wave), red its reduction LDS.
-template <int FMT, bool XF16, int KF, int SD, class TB>
+// EPI: 0 none, 1 bias / residual (tb.ep), 2 SwiGLU with tb.ep.W2: the
+// workgroup then takes each of its tiles twice, gate rows (virtual tile 2n)
+// then the same up rows (2n + 1), and writes silu(gate) * up.
+template <int FMT, bool XF16, int KF, int SD, int EPI = 0, class TB>
 __device__ __forceinline__ void mfma_segment(const TB& tb, const MSeg& sg, uint32_t* stage, float* red) {
   constexpr int MW = kMaxWaves<KF>;
   const MfmaArgs a{sg.W, sg.off1, sg.off2, sg.off3, sg.x, sg.y, sg.N, tb.K, tb.nv, tb.waves};
@@ -423,6 +452,9 @@ __device__ __forceinline__ void mfma_segment(const TB& tb, const MSeg& sg, uint3
   const int64_t xrow = int64_t(min(vec, a.nv - 1)) * K;  // address stays inside x for padding parts
   const int ntiles = (N + 15) >> 4;
   const Staging<FMT> stg{a, U, K >> 8, lane};
+  MfmaArgs a2 = a;
+  if constexpr (EPI == 2) a2.W = tb.ep.W2;  // same format, shape and plane offsets
+  const Staging<FMT> stg2{a2, U, K >> 8, lane};
 
   uint32_t* lds = stage + wave * SD;
 
@@ -437,9 +469,18 @@ __device__ __forceinline__ void mfma_segment(const TB& tb, const MSeg& sg, uint3
   // operands (the kernels spilled): one set is refilled with the following
   // chunk.
   constexpr bool TWO = KF == 8 && FMT != QMV_Q6K;
-  int tile = bid;  // < ntiles (a segment has at most as many workgroups as tiles)
-  const int ntl = (ntiles - bid + nblk - 1) / nblk;  // tiles of this workgroup
-  Stage<FMT> SA = stg.load(tile, u0), SB;
+  // this workgroup's tiles bid, bid + nblk, ... (a segment has at most as many
+  // workgroups as tiles); with SwiGLU each twice (virtual tiles n = 2i, 2i + 1)
+  constexpr int VT = EPI == 2 ? 2 : 1;
+  const int ntl = VT * ((ntiles - bid + nblk - 1) / nblk);  // virtual tiles of this workgroup
+  auto tile_of = [&](int n) { return bid + (n / VT) * nblk; };
+  auto vload = [&](int n, int u) -> Stage<FMT> {
+    if constexpr (EPI == 2) {
+      if (n & 1) return stg2.load(tile_of(n), u);
+    }
+    return stg.load(tile_of(n), u);
+  };
+  Stage<FMT> SA = vload(0, u0), SB;
 
   // ---- A operands of this wave's K slice, built once (zero past K and for
   // vectors >= nv, so those fragments and parts contribute nothing)
@@ -499,32 +540,47 @@ __device__ __forceinline__ void mfma_segment(const TB& tb, const MSeg& sg, uint3
   }
 
   if constexpr (TWO) {
-    if (ntl > 1) SB = stg.load(tile + nblk, u0);
+    if (ntl > 1) SB = vload(1, u0);
   }
 
   int buf = 0;
   float acc0, acc1;  // vectors 2G and 2G + 1 of weight row (lane & 15)
-  // the W partial sums of a tile meet in LDS, added in wave order
-  auto finish = [&]() {
+  float gate[2];     // SwiGLU: the gate totals of this thread's outputs, until the up tile
+  // the W partial sums of (virtual) tile n meet in LDS, added in wave order
+  auto finish = [&](int n) {
     float* rb = red + (buf * MW + wave) * 128;
     rb[2 * lane] = acc0;
     rb[2 * lane + 1] = acc1;
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    for (int t = threadIdx.x; t < 128; t += 64 * a.waves) {  // (blockDim.x: reading it adds ~256 bytes of hidden kernel arguments)
+    const int tile = tile_of(n);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {  // (blockDim.x: reading it adds ~256 bytes of hidden kernel arguments)
+      const int t = threadIdx.x + j * 64 * a.waves;
+      if (t >= 128) break;
       const int i = t & 15;  // weight row within the tile
       const int v = t >> 4;  // vector
       const int src = 2 * (i + 16 * (v >> 1)) + (v & 1);
       float s = 0.0f;
       for (int w = 0; w < a.waves; ++w) s += red[(buf * MW + w) * 128 + src];
       const int r = tile * 16 + i;
+      const int rc = min(r, N - 1);
+      if constexpr (EPI == 2) {
+        if ((n & 1) == 0) {
+          gate[j] = s;
+          continue;
+        }
+        s = silu_mul(gate[j], s);
+      } else if constexpr (EPI == 1) {
+        if (tb.ep.bias) s += tb.ep.bias[rc];
+        if (tb.ep.res) s = tb.ep.res[int64_t(min(v, a.nv - 1)) * N + rc] + s;
+      }
       if (v < a.nv && r < N) a.y[int64_t(v) * N + r] = s;
     }
     buf ^= 1;
-    tile += nblk;
   };
   if constexpr (!TWO) {
     const int nch = (min(KF, U - u0) + 7) >> 3;  // chunks of this wave (1 or 2)
-    for (;;) {
+    for (int n = 0;; ++n) {
       acc0 = acc1 = 0.0f;
 #pragma unroll
       for (int c = 0; c < KF / 8; ++c) {
@@ -533,13 +589,13 @@ __device__ __forceinline__ void mfma_segment(const TB& tb, const MSeg& sg, uint3
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         const Stage<FMT> cur = SA;
         // next chunk: the following one of this tile, else the first of the next tile
-        if (c + 1 < nch) SA = stg.load(tile, u0 + 8 * (c + 1));
-        else if (tile + nblk < ntiles) SA = stg.load(tile + nblk, u0);
+        if (c + 1 < nch) SA = vload(n, u0 + 8 * (c + 1));
+        else if (n + 1 < ntl) SA = vload(n + 1, u0);
         stg.compute(cur, lds, A + 8 * c, u0 + 8 * c, acc0, acc1);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // operand reads done before the next store
       }
-      finish();
-      if (tile >= ntiles) return;
+      finish(n);
+      if (n + 1 >= ntl) return;
     }
   } else {
     // tile number n of this workgroup from set S, which then takes tile n + 2
@@ -548,10 +604,10 @@ __device__ __forceinline__ void mfma_segment(const TB& tb, const MSeg& sg, uint3
       stg.store(S, lds);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       const Stage<FMT> cur = S;  // its loads are done: a plain copy
-      if (n + 2 < ntl) S = stg.load(tile + 2 * nblk, u0);
+      if (n + 2 < ntl) S = vload(n + 2, u0);
       stg.compute(cur, lds, A, u0, acc0, acc1);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // operand reads done before the next store
-      finish();
+      finish(n);
     };
     for (int n = 0;; n += 2) {
       run(SA, n);
@@ -584,6 +640,15 @@ __global__ __launch_bounds__(64 * kMaxWaves<KF>) void matvec_mfma_kernel(const M
   }
 }
 
+// One matvec with a fused epilogue (EPI 1: bias / residual, 2: SwiGLU).
+template <int FMT, bool XF16, int KF, int EPI>
+__global__ __launch_bounds__(64 * kMaxWaves<KF>) void matvec_mfma_epi_kernel(const MTableEpi tb) {
+  constexpr int MW = kMaxWaves<KF>;
+  __shared__ uint32_t stage_lds[MW * kStageDw<FMT>];
+  __shared__ f32x4 red_raw[2][MW][32];
+  mfma_segment<FMT, XF16, KF, kStageDw<FMT>, EPI>(tb, tb.s[0], stage_lds, reinterpret_cast<float*>(red_raw));
+}
+
 int blocks_override() {
   static const int v = [] {
     return ab_switch("QMV_MFMA_BLOCKS", 0);  // A/B tuning only: workgroups per launch
@@ -602,7 +667,7 @@ int blocks_override() {
 // gate+up 11.0 -> 8.6 us).  Q6K keeps one register set, so its tiles run back
 // to back: the 32000 x 2048 head took 22.1 us at 512 and 25.8 at 256.
 template <int FMT, bool XF16, int KF>
-hipError_t go(MTable& t, hipStream_t s) {
+hipError_t go(MTable& t, hipStream_t s, const MEpi* ep = nullptr) {
   int64_t tiles[kMaxSeg], total = 0;
   for (int i = 0; i < t.count; ++i) {
     tiles[i] = (t.s[i].N + 15) / 16;
@@ -620,6 +685,15 @@ hipError_t go(MTable& t, hipStream_t s) {
   }
   for (int i = 0; i < kMaxSeg; ++i) t.first[i] = i < t.count ? t.s[i].b0 : INT_MAX;  // INT_MAX: never selected
   const dim3 grid(b), block(64 * t.waves);
+  if constexpr (FMT != kMixM) {
+    if (ep) {
+      if (ep->W2)
+        hipLaunchKernelGGL((matvec_mfma_epi_kernel<FMT, XF16, KF, 2>), grid, block, 0, s, with_epi(t, *ep));
+      else
+        hipLaunchKernelGGL((matvec_mfma_epi_kernel<FMT, XF16, KF, 1>), grid, block, 0, s, with_epi(t, *ep));
+      return hipGetLastError();
+    }
+  }
   if (t.count == 1 && FMT != kMixM)
     hipLaunchKernelGGL((matvec_mfma_kernel<FMT, XF16, KF, 1>), grid, block, 0, s, shrink<1>(t));
   else if (t.count <= 4)
@@ -630,7 +704,7 @@ hipError_t go(MTable& t, hipStream_t s) {
 }
 
 template <int FMT, bool XF16>
-bool pick_kf(MTable& t, hipStream_t s, hipError_t* err) {
+bool pick_kf(MTable& t, hipStream_t s, hipError_t* err, const MEpi* ep = nullptr) {
   const int U = t.K / 32;
   // fragments per wave, a multiple of 8 (whole Q4K / Q6K super-blocks, W4A16
   // group pairs): 8 up to K = 2048 (at most 8 waves), else 16 (at most 12 waves,
@@ -638,20 +712,20 @@ bool pick_kf(MTable& t, hipStream_t s, hipError_t* err) {
   const int kf = U <= 8 * kMaxWaves<8> ? 8 : 16;
   t.waves = (U + kf - 1) / kf;
   if (t.waves > (kf == 8 ? kMaxWaves<8> : kMaxWaves<16>)) return false;
-  *err = kf == 8 ? go<FMT, XF16, 8>(t, s) : go<FMT, XF16, 16>(t, s);
+  *err = kf == 8 ? go<FMT, XF16, 8>(t, s, ep) : go<FMT, XF16, 16>(t, s, ep);
   return true;
 }
 
-bool launch_table(int fmt, MTable& t, int x_dtype, hipStream_t s, hipError_t* err) {
+bool launch_table(int fmt, MTable& t, int x_dtype, hipStream_t s, hipError_t* err, const MEpi* ep = nullptr) {
   if (x_dtype == QMV_Q8X) return false;  // 8-bit activations run on the general kernel
   const bool f16 = (x_dtype == QMV_F16);
   switch (fmt) {
-    case QMV_Q8_0: return pick_kf<QMV_Q8_0, false>(t, s, err);
+    case QMV_Q8_0: return pick_kf<QMV_Q8_0, false>(t, s, err, ep);
     case QMV_W4A16_G64:
-      return f16 ? pick_kf<QMV_W4A16_G64, true>(t, s, err) : pick_kf<QMV_W4A16_G64, false>(t, s, err);
-    case QMV_Q4K: return pick_kf<QMV_Q4K, false>(t, s, err);
-    case QMV_Q6K: return pick_kf<QMV_Q6K, false>(t, s, err);
-    case kMixM: return pick_kf<kMixM, false>(t, s, err);
+      return f16 ? pick_kf<QMV_W4A16_G64, true>(t, s, err, ep) : pick_kf<QMV_W4A16_G64, false>(t, s, err, ep);
+    case QMV_Q4K: return pick_kf<QMV_Q4K, false>(t, s, err, ep);
+    case QMV_Q6K: return pick_kf<QMV_Q6K, false>(t, s, err, ep);
+    case kMixM: return ep ? false : pick_kf<kMixM, false>(t, s, err);
     default: return false;
   }
 }
@@ -672,6 +746,15 @@ bool fits(int fmt, int64_t N, int64_t K) {
 // shapes outside this kernel's range (K > 6144, packed matrix >= 2 GiB).
 bool launch_matvec_mfma(int fmt, int64_t N, int64_t K, int nv, const uint8_t* W, const void* x, int x_dtype,
                         float* y, hipStream_t s, hipError_t* err) {
+  return launch_matvec_mfma_epi(fmt, N, K, nv, W, nullptr, x, x_dtype, y, nullptr, nullptr, s, err);
+}
+
+// The same with a fused epilogue: W2 != null runs SwiGLU (y = silu(W x) *
+// (W2 x)), otherwise y = res + (W x + bias) (bias [N], res [nv][N], either
+// null).  All null: the plain kernel.
+bool launch_matvec_mfma_epi(int fmt, int64_t N, int64_t K, int nv, const uint8_t* W, const uint8_t* W2,
+                            const void* x, int x_dtype, float* y, const float* bias, const float* res,
+                            hipStream_t s, hipError_t* err) {
   if (!has_kernel(fmt) || !fits(fmt, N, K)) return false;
   const Planes p = planes_of(fmt, N, K);
   MTable t{};
@@ -679,7 +762,9 @@ bool launch_matvec_mfma(int fmt, int64_t N, int64_t K, int nv, const uint8_t* W,
   t.K = int(K);
   t.nv = nv;
   t.s[0] = MSeg{W, p.off[1], p.off[2], p.off[3], x, y, int(N), 0, 0, fmt};
-  return launch_table(fmt, t, x_dtype, s, err);
+  if (!W2 && !bias && !res) return launch_table(fmt, t, x_dtype, s, err);
+  const MEpi ep{W2, bias, res};
+  return launch_table(fmt, t, x_dtype, s, err, &ep);
 }
 
 // Several matvecs of one K and batch (>= 2) on the matrix cores: per chunk of

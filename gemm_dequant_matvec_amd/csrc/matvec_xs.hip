@@ -496,7 +496,6 @@ __device__ __forceinline__ void store_y(rsrc_t ry, int row, bool ok, float v) {
 // the same rows of both matrices (ep.W2 is the up matrix) and the epilogue
 // combines the two totals.  Otherwise bias and residual (null: none) are
 // added to each total in the epilogue.
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
 template <int FMT, bool XF16, int LPR, int UPL, int R, int KS, bool DB, bool PAIR = false>
 __device__ __forceinline__ void xs_segment(const Seg& sg, const int K, const Epi& ep) {

@@ -100,6 +100,10 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits) {
   return __builtin_bit_cast(float, bits << 16);
 }
 
+// SwiGLU's product of one output: silu(g) * u with silu(g) = g / (1 + e^-g)
+// (f32; expf is the device library's).
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
 // ------------------------------------------------------- A/B tuning switches
 // Kernel-configuration switches read from the environment exist only in
 // measurement builds (-DQMV_AB_SWITCHES=1).  The shipped library is built
@@ -139,6 +143,9 @@ hipError_t launch_matvec_epi(int fmt, int64_t N, int64_t K, int64_t batch, const
                              hipStream_t s);
 bool launch_matvec_mfma(int fmt, int64_t N, int64_t K, int nv, const uint8_t* W, const void* x, int x_dtype,
                         float* y, hipStream_t s, hipError_t* err);
+bool launch_matvec_mfma_epi(int fmt, int64_t N, int64_t K, int nv, const uint8_t* W, const uint8_t* W2,
+                            const void* x, int x_dtype, float* y, const float* bias, const float* res,
+                            hipStream_t s, hipError_t* err);
 bool launch_matvec_grouped_mfma(int fmt, int64_t K, int64_t batch, int count, const qmv_matvec_item* items,
                                 int x_dtype, hipStream_t s, hipError_t* err);
 bool launch_matvec_grouped_b1(int fmt, int64_t K, int count, const qmv_matvec_item* items, int x_dtype,

@@ -6,7 +6,9 @@ matrices (aot-llm README, Metal backend notes).  References: the oracle's
 epilogue_ref / swiglu_ref in f64 over the exact dequantized weights, with
 the matvec bound propagated (epilogue_bound, swiglu_bound).  Shapes reach
 the streaming kernel's lanes-per-row settings (16 / 32 / 64 lanes, K split
-over waves) at batch 1 and the FMA kernel at batch 2..11.
+over waves) at batch 1, and at batch 2..11 the matrix-core kernel (Q8_0,
+W4A16, Q4K, Q6K: one to eleven waves per workgroup, one or two K chunks per
+wave) or the FMA kernel (the other formats).
 """
 import numpy as np
 import pytest
@@ -32,7 +34,7 @@ def _prod(fmt, w, x, xd):
     return oracle.matvec_ref(W32, xv), oracle.tolerance_bound(W32, xv, TAU)
 
 
-SHAPES = [(130, 512), (200, 1024), (129, 2048), (70, 5632)]
+SHAPES = [(100, 256), (130, 512), (200, 1024), (129, 2048), (70, 5632)]
 
 
 @pytest.mark.parametrize("fmt", ["q4k", "q6k", "w4a16_g64", "q8_0", "q5k", "i8row"])
@@ -83,14 +85,16 @@ def test_swiglu(qmv, fmt, batch):
         assert r["ok"], (fmt, N, K, batch, r)
 
 
-def test_swiglu_decoder_mlp_shape_and_graph(qmv):
-    # the 1.1B decoder's gate / up (5632 x 2048, Q4K), fused, captured in a graph
+@pytest.mark.parametrize("batch", [1, 8])
+def test_swiglu_decoder_mlp_shape_and_graph(qmv, batch):
+    # the 1.1B decoder's gate / up (5632 x 2048, Q4K), fused, captured in a
+    # graph; at batch 8 on the matrix cores, several row tiles per workgroup
     fmt, N, K = "q4k", 5632, 2048
     wg = wl.gen_weights(fmt, N, K, (64, 0, 4))
     wu = wl.gen_weights(fmt, N, K, (64, 0, 5))
-    x = wl.gen_x(K, 1, "f32", (64, 0, 4))
+    x = wl.gen_x(K, batch, "f32", (64, 0, 4))
     Wg, Wu, xd = pack_dev(qmv, fmt, wg), pack_dev(qmv, fmt, wu), dev_x(x, "f32")
-    h = torch.empty((1, N), dtype=torch.float32, device="cuda")
+    h = torch.empty((batch, N), dtype=torch.float32, device="cuda")
     qmv.matvec_swiglu(fmt, Wg, Wu, xd, N, K, h=h)
     torch.cuda.synchronize()
     eager = h.clone()
