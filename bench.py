@@ -27,7 +27,7 @@ median of 3, dequantization and product split, and one BLAS thread).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--copies C]
                        [--no-extras] [--no-cpu-baseline] [--cpu-quick] [--leg NAME]
-(--leg runs one extras workload alone and prints its result, for profiling.)
+(--leg runs extras workloads alone and prints their results, for profiling.)
 """
 from __future__ import annotations
 
@@ -67,7 +67,8 @@ def parse():
     p.add_argument("--cpu-quick", action="store_true",
                    help="skip the oracle's decode-token run (c5) in the CPU baseline")
     p.add_argument("--leg", default=None,
-                   help="run only this extras workload and print its result (profiling); one of: "
+                   help="run only these extras workloads (comma-separated) and print their results "
+                        "(profiling); of: "
                         + ", ".join(LEGS))
     return p.parse_args()
 
@@ -398,6 +399,7 @@ def leg_sweep_fused(qmv, b):
 
 LEGS = {
     "platform_probes": platform_probes,
+    "copy_probe_1GiB": lambda q: copy_probe(),
     "q8_0_512x512_b1_single": leg_q8_0,
     "q4k_0.6B_mlp_b1_cold": leg_mlp06,
     "q4k_vocab_head_151936x1024_b1_cold": leg_head06,
@@ -761,10 +763,12 @@ def main():
     assert torch.cuda.is_available(), "no GPU visible"
     torch.cuda.set_device(0)
     if args.leg is not None:
-        if args.leg not in LEGS:
-            print(f"unknown leg {args.leg!r}; one of {', '.join(LEGS)}", file=sys.stderr)
-            sys.exit(2)
-        print(json.dumps({"leg": args.leg, "result": LEGS[args.leg](qmv)}), flush=True)
+        for leg in args.leg.split(","):
+            if leg not in LEGS:
+                print(f"unknown leg {leg!r}; one of {', '.join(LEGS)}", file=sys.stderr)
+                sys.exit(2)
+        for leg in args.leg.split(","):
+            print(json.dumps({"leg": leg, "result": LEGS[leg](qmv)}), flush=True)
         return
 
     log("headline: W4A16 g64 1.1B MLP matvecs, batch 1, copies", args.copies)

@@ -6,6 +6,15 @@
         durations plus HBM bytes per dispatch from a --pmc FETCH_SIZE run and a
         --pmc WRITE_SIZE run -> profiles/NAME.md and the NAME record of
         profiles/traffic.json (read by bench.py)
+    python profile_summary.py pmc NAME KERNEL_REGEX TRACE_DIR "COMMANDS ..." PMC_DIR [PMC_DIR ...]
+        kernel durations plus the median per dispatch of every counter collected
+        in the --pmc runs, for the kernels whose name matches KERNEL_REGEX, with
+        the derived MFMA figures -> profiles/NAME.md
+
+Options: --note TEXT (a paragraph under the title); --span REGEX --replays R
+(trace mode: the union of the busy intervals of the dispatches matching REGEX
+against the sum of their durations, per replay, to reconcile with an
+event-timed step).
 
 FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what they read for
 the 1 GiB device copy that bench.py runs as its copy probe (1 GiB read and
@@ -72,6 +81,41 @@ def counters(pmc_dir: str, counter: str):
     return out
 
 
+def counters_all(pmc_dir: str, kregex: str):
+    """{counter: [values per matching dispatch]}."""
+    out = {}
+    with open(_one("*counter_collection.csv", pmc_dir)) as f:
+        for r in csv.DictReader(f):
+            if re.search(kregex, r["Kernel_Name"]):
+                out.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def span(trace_dir: str, regex: str, replays: int) -> list[str]:
+    """Sum of durations vs union of busy intervals of the dispatches matching regex."""
+    iv = []
+    with open(_one("*kernel_trace.csv", trace_dir)) as f:
+        for r in csv.DictReader(f):
+            if re.search(regex, r["Kernel_Name"]):
+                iv.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    iv.sort()
+    total = sum(b - a for a, b in iv)
+    union, cur = 0, None
+    for a, b in iv:
+        if cur is None or a > cur[1]:
+            if cur:
+                union += cur[1] - cur[0]
+            cur = [a, b]
+        else:
+            cur[1] = max(cur[1], b)
+    if cur:
+        union += cur[1] - cur[0]
+    return ["", f"## Busy time of the dispatches matching `{regex}`", "",
+            f"{len(iv)} dispatches over {replays} replays: sum of durations {total / replays / 1e3:.1f} us "
+            f"per replay; union of their busy intervals {union / replays / 1e3:.1f} us per replay "
+            f"(dispatches overlap by {100 * (1 - union / total):.1f} % of the summed durations)."]
+
+
 def source_sha() -> str:
     h = hashlib.sha256()
     for f in SOURCES:
@@ -96,11 +140,57 @@ def main(argv):
     md = [f"# rocprofv3 summary: {name}", ""]
     if note:
         md += [note, ""]
+    sp = None
+    if "--span" in argv:
+        i = argv.index("--span")
+        sp = (argv[i + 1], int(argv[argv.index("--replays") + 1]))
+        j = argv.index("--replays")
+        argv = [a for k, a in enumerate(argv) if k not in (i, i + 1, j, j + 1)]
     if mode == "trace":
         trace_dir, cmd = argv[2], argv[3]
         md += ["Commands (run from the repository root on one MI355X):", "", "```", "cd /tmp && export TMPDIR=/tmp",
                cmd, "```", "", "## Kernel durations (--kernel-trace --stats)", ""]
         md += duration_table(durations(trace_dir))
+        if sp:
+            md += span(trace_dir, *sp)
+    elif mode == "pmc":
+        kre, trace_dir, cmds, dirs = argv[2], argv[3], argv[4], argv[5:]
+        md += ["Commands (run from the repository root on one MI355X):", "", "```", "cd /tmp && export TMPDIR=/tmp",
+               *cmds.split(" ;; "), "```", "", "## Kernel durations (--kernel-trace --stats)", ""]
+        rows = durations(trace_dir)
+        md += duration_table(rows)
+        c = {}
+        for d in dirs:
+            c.update(counters_all(d, kre))
+        med = {k: statistics.median(v) for k, v in c.items()}
+        md += ["", f"## Counters per dispatch of `{kre}` (median over {max(len(v) for v in c.values())} dispatches)",
+               "", "| counter | value |", "|---|---|"]
+        md += [f"| {k} | {v:.0f} |" for k, v in sorted(med.items())]
+        der = []
+        dur = [a for n, _, a, *_ in rows if re.search(kre, n)]
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in med:
+            fl = med["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+            der.append(f"bf16 MFMA flops per dispatch (MOPS x 512): {fl:.4g}")
+            if dur:
+                der.append(f"at the traced average duration {dur[0]:.0f} ns: {fl / dur[0] / 1e3:.1f} TFLOP/s, "
+                           f"{fl / dur[0] / 1e3 / 2500:.3f} of the 2.5 PFLOP/s dense bf16 peak")
+        simd_cycles = 1024 * dur[0] * 2.4 if dur else None  # 256 CUs x 4 SIMDs at 2.4 GHz, over the duration
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in med and simd_cycles:
+            der.append(f"MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES (summed over SIMDs) / (1024 SIMDs x duration x "
+                       f"2.4 GHz) = {med['SQ_VALU_MFMA_BUSY_CYCLES'] / simd_cycles:.3f}; busy cycles per MFMA "
+                       f"instruction {med['SQ_VALU_MFMA_BUSY_CYCLES'] / max(1, med.get('SQ_INSTS_MFMA', 1)):.1f}")
+        if "SQ_INSTS_VALU" in med and "SQ_INSTS_MFMA" in med and med["SQ_INSTS_MFMA"]:
+            other = med["SQ_INSTS_VALU"] - med["SQ_INSTS_MFMA"]
+            der.append(f"VALU instructions other than MFMA: {other / med['SQ_INSTS_MFMA']:.2f} per MFMA instruction"
+                       + (f"; at 4 cycles per wave64 VALU instruction they fill "
+                          f"{4 * other / simd_cycles:.3f} of the SIMD cycles" if simd_cycles else ""))
+        if "SQ_INSTS_LDS" in med and "SQ_INSTS_MFMA" in med and med["SQ_INSTS_MFMA"]:
+            der.append(f"LDS instructions per MFMA instruction: {med['SQ_INSTS_LDS'] / med['SQ_INSTS_MFMA']:.2f}"
+                       + (f"; bank conflicts (SQ_LDS_BANK_CONFLICT cycles) per LDS instruction "
+                          f"{med['SQ_LDS_BANK_CONFLICT'] / med['SQ_INSTS_LDS']:.2f}"
+                          if "SQ_LDS_BANK_CONFLICT" in med and med["SQ_INSTS_LDS"] else ""))
+        if der:
+            md += ["", "Derived:", ""] + [f"- {d}" for d in der]
     elif mode == "traffic":
         trace_dir, fetch_dir, write_dir, cmds = argv[2], argv[3], argv[4], argv[5]
         fetch = counters(fetch_dir, "FETCH_SIZE")
