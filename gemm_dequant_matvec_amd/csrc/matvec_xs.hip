@@ -497,7 +497,9 @@ __device__ __forceinline__ void store_y(rsrc_t ry, int row, bool ok, float v) {
 // combines the two totals.  Otherwise bias and residual (null: none) are
 // added to each total in the epilogue.
 
-template <int FMT, bool XF16, int LPR, int UPL, int R, int KS, bool DB, bool PAIR = false>
+// EPI: the bias / residual epilogue (a kernel of its own, so that the plain
+// kernels carry none of its registers).
+template <int FMT, bool XF16, int LPR, int UPL, int R, int KS, bool DB, bool PAIR = false, bool EPI = false>
 __device__ __forceinline__ void xs_segment(const Seg& sg, const int K, const Epi& ep) {
   constexpr int NM = PAIR ? 2 : 1;           // matrices read per row group
   constexpr int TPB = KS == 1 ? kWaves : 1;  // independent lane-group teams per block
@@ -515,17 +517,19 @@ __device__ __forceinline__ void xs_segment(const Seg& sg, const int K, const Epi
     g2 = Geo{make_rsrc(ep.W2, sg.nrec[0]), make_rsrc(ep.W2 + sg.off1, sg.nrec[1]),
              make_rsrc(ep.W2 + sg.off2, sg.nrec[2]), make_rsrc(ep.W2 + sg.off3, sg.nrec[3]), K};
   const int N = sg.N;
-  // the value stored for row `row` from its total(s) (row is clamped for the
-  // epilogue loads; the store itself is predicated)
-  auto finish = [&](int row, float tot, float tot2) -> float {
+  // the value stored from a row's total(s); eb / er: its bias and residual,
+  // loaded with the row group's weights (load_epi) so that their latency is
+  // not added at the end
+  auto finish = [&](float tot, float tot2, float eb, float er) -> float {
     if constexpr (PAIR) {
       return silu_mul(tot, tot2);
-    } else {
-      const int rc = row < N ? row : N - 1;
+    } else if constexpr (EPI) {
       float v = tot;
-      if (ep.bias) v += ep.bias[rc];
-      if (ep.res) v = ep.res[rc] + v;
+      if (ep.bias) v += eb;
+      if (ep.res) v = er + v;
       return v;
+    } else {
+      return tot;
     }
   };
   const rsrc_t ry = make_rsrc(sg.y, uint32_t(N) * 4u);
@@ -590,9 +594,24 @@ __device__ __forceinline__ void xs_segment(const Seg& sg, const int K, const Epi
         for (int j = 0; j < UPL; ++j) dst[m][r][j] = load_raw<FMT>(m ? g2 : g, row, uu[j], row < N && uv[j]);
       }
   };
+  // bias / residual of a row group's rows (row r * RPW + sub of the group;
+  // rows past the end clamped), issued after its weights
+  float eba[R], era[R], ebb[R], erb[R];
+  auto load_epi = [&](float (&eb)[R], float (&er)[R], int gi) {
+    if constexpr (EPI) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int rc = min(gi * (R * RPW) + r * RPW + sub, N - 1);
+        eb[r] = ep.bias ? ep.bias[rc] : 0.0f;
+        er[r] = ep.res ? ep.res[rc] : 0.0f;
+      }
+    }
+  };
   int grp = gw;
   load_group(ga, grp);
   if constexpr (DB) load_group(gb, grp + TW);
+  load_epi(eba, era, grp);
+  if constexpr (DB) load_epi(ebb, erb, grp + TW);
 
   // 3. activation slices into registers (and the per-unit sums)
   XUnit<H2> xs[UPL];
@@ -620,7 +639,7 @@ __device__ __forceinline__ void xs_segment(const Seg& sg, const int K, const Epi
     for (int j = 0; j < UPL; ++j) load_x<FMT, XF16>(xs[j], nullptr, 0, uv[j], &xr[j]);
   }
 
-  auto do_group = [&](const Raw<FMT> (&cur)[NM][R][UPL], int gi) {
+  auto do_group = [&](const Raw<FMT> (&cur)[NM][R][UPL], int gi, const float (&eb)[R], const float (&er)[R]) {
     float acc[NM][R];
 #pragma unroll
     for (int m = 0; m < NM; ++m)
@@ -643,7 +662,13 @@ __device__ __forceinline__ void xs_segment(const Seg& sg, const int K, const Epi
       const bool first = lane % (64 / R) == 0;
       const int row = gi * R + r;
       if constexpr (KS == 1) {
-        store_y(ry, row, first && row < N, finish(row, tot, tot2));
+        float b = eb[0], e = er[0];  // this lane's row r (a select, not a dynamic register index)
+#pragma unroll
+        for (int i = 1; i < R; ++i) {
+          b = r == i ? eb[i] : b;
+          e = r == i ? er[i] : e;
+        }
+        store_y(ry, row, first && row < N, finish(tot, tot2, b, e));
       } else {
         if (first) {
           red[par][ks][r] = tot;
@@ -657,7 +682,7 @@ __device__ __forceinline__ void xs_segment(const Seg& sg, const int K, const Epi
         const float tot2 = PAIR ? group_sum<LPR>(acc[NM - 1][r], sub) : 0.0f;
         const int row = gi * (R * RPW) + r * RPW + sub;
         if constexpr (KS == 1) {
-          store_y(ry, row, l == 0 && row < N, finish(row, tot, tot2));
+          store_y(ry, row, l == 0 && row < N, finish(tot, tot2, eb[r], er[r]));
         } else {
           if (l == 0) {
             red[par][ks][r * RPW + sub] = tot;
@@ -677,7 +702,7 @@ __device__ __forceinline__ void xs_segment(const Seg& sg, const int K, const Epi
           t += red[par][w][r * RPW + sub];
           if constexpr (PAIR) t2 += red[par][w][RPW * R + r * RPW + sub];
         }
-        store_y(ry, row, ks == 0 && l == 0 && row < N, finish(row, t, t2));
+        store_y(ry, row, ks == 0 && l == 0 && row < N, finish(t, t2, eb[r], er[r]));
       }
       par ^= 1;  // the next group writes the other buffer while this one is read
     }
@@ -686,15 +711,17 @@ __device__ __forceinline__ void xs_segment(const Seg& sg, const int K, const Epi
     // a set is refilled as soon as it has been used, so the other set's loads
     // are always in flight while one group is computed
     while (grp < ngroups) {
-      do_group(ga, grp);
+      do_group(ga, grp, eba, era);
       load_group(ga, grp + 2 * TW);
+      load_epi(eba, era, grp + 2 * TW);
       if (grp + TW >= ngroups) break;
-      do_group(gb, grp + TW);
+      do_group(gb, grp + TW, ebb, erb);
       load_group(gb, grp + 3 * TW);
+      load_epi(ebb, erb, grp + 3 * TW);
       grp += 2 * TW;
     }
   } else {  // at most one group per wave (the launcher checks)
-    if (grp < ngroups) do_group(ga, grp);
+    if (grp < ngroups) do_group(ga, grp, eba, era);
   }
 }
 
@@ -712,6 +739,12 @@ __global__ __launch_bounds__(KS == 1 ? kThreads : 64 * KS) void matvec_xs_kernel
     for (int i = 1; i < CAP; ++i) si += int(blockIdx.x) >= t.first[i] ? 1 : 0;
   }
   xs_segment<FMT, XF16, LPR, UPL, R, KS, DB>(t.s[si], t.K, t.ep);
+}
+
+// One matvec with the bias / residual epilogue (t.ep).
+template <int FMT, bool XF16, int LPR, int UPL, int R, int KS, bool DB>
+__global__ __launch_bounds__(KS == 1 ? kThreads : 64 * KS) void matvec_xs_epi_kernel(const SegTableT<1> t) {
+  xs_segment<FMT, XF16, LPR, UPL, R, KS, DB, false, true>(t.s[0], t.K, t.ep);
 }
 
 // SwiGLU of one gate / up pair: one segment (the gate), ep.W2 the up matrix.
@@ -788,6 +821,8 @@ hipError_t go(SegTable& t, hipStream_t s) {
         // two matrices' registers per row group: at most two rows x units per lane
         if constexpr (R * UPL <= 2)
           hipLaunchKernelGGL((matvec_xs_pair_kernel<FMT, XF16, LPR, UPL, R, KS, DB>), grid, block, 0, s, shrink<1>(t));
+      } else if (t.ep.bias || t.ep.res) {  // a single matrix
+        hipLaunchKernelGGL((matvec_xs_epi_kernel<FMT, XF16, LPR, UPL, R, KS, DB>), grid, block, 0, s, shrink<1>(t));
       } else if (t.count == 1)
         hipLaunchKernelGGL((matvec_xs_kernel<FMT, XF16, LPR, UPL, R, 1, KS, DB>), grid, block, 0, s, shrink<1>(t));
       else if (t.count <= 4)
