@@ -650,7 +650,8 @@ def _oracle_matvecs(oracle, mats, reps=1):
 def cpu_baseline(args):
     """The oracle, untuned, on the host: numpy f32 dequantization (one thread)
     and the f64 product (BLAS, as many threads as cores this process may use).
-    Per config the median of 3 runs (1 for the decode token), split into
+    Per config the median of 3 runs (the decode token: 3 when one takes under
+    5 s, else 1), split into
     dequantization and product time; c1-c3 also with one BLAS thread.  Inputs
     are generated before timing.  `value` is the headline workload's rate."""
     import statistics
@@ -705,13 +706,22 @@ def cpu_baseline(args):
             for name, fmt, N, K, key in cfg["mats"]:
                 counts[(fmt, N, K)] = counts.get((fmt, N, K), 0) + 1
                 first.setdefault((fmt, N, K), key)
-            t_dq = t_mv = 0.0
-            for (fmt, N, K), key in first.items():
-                m = [(fmt, wl.gen_weights(fmt, N, K, key), wl.gen_x(K, 1, "f32", key), "f32")]
-                a, b = _oracle_matvecs(oracle, m, reps=counts[(fmt, N, K)])
-                t_dq, t_mv = t_dq + a, t_mv + b
-            per["c5_decode_token_1.1B_b1"] = {"s": t_dq + t_mv, "dequant_s": t_dq, "product_s": t_mv, "runs": 1,
-                                              "tok_per_s": 1.0 / (t_dq + t_mv),
+            shapes = [(fmt, wl.gen_weights(fmt, N, K, key), wl.gen_x(K, 1, "f32", key), "f32")
+                      for (fmt, N, K), key in first.items()]
+
+            def token():
+                t_dq = t_mv = 0.0
+                for m in shapes:
+                    N, K = m[1]["q"].shape
+                    a, b = _oracle_matvecs(oracle, [m], reps=counts[(m[0], N, K)])
+                    t_dq, t_mv = t_dq + a, t_mv + b
+                return t_dq, t_mv
+            runs = [token()]
+            if sum(runs[0]) < 5.0:  # a fast host: the median of 3 still fits the time budget
+                runs += [token(), token()]
+            t_dq, t_mv = sorted(runs, key=sum)[len(runs) // 2]
+            per["c5_decode_token_1.1B_b1"] = {"s": t_dq + t_mv, "dequant_s": t_dq, "product_s": t_mv,
+                                              "runs": len(runs), "tok_per_s": 1.0 / (t_dq + t_mv),
                                               "gbs": cfg_bytes(cfg) / (t_dq + t_mv) / 1e9}
     one = {}
     with threadpool_limits(limits=1):
