@@ -362,6 +362,46 @@ def leg_head06(qmv):
                        st.bytes / (ms * 1e-3) / 1e9)
 
 
+def leg_stream_ramp(qmv):
+    """Launch time against launch size: the grouped W4A16 gate+up launch (two
+    matrices of 5632 c x 2048, fp16 x, batch 1) at c = 1, 2, 4, 8, over enough
+    cold copies to stream >= 700 MB per graph.  The line t = t0 + bytes / bw
+    fitted to the per-launch times splits a launch into a fixed part (launch,
+    first-load latency, drain) and the steady streaming rate."""
+    import numpy as np
+    import torch
+    import workloads as wl
+    K, pts = 2048, []
+    for c in (1, 2, 4, 8):
+        N = 5632 * c
+        mats = []
+        for i in range(2):
+            w = wl.gen_weights("w4a16_g64", N, K, (9, c, i))
+            mats.append(qmv.pack("w4a16_g64", {k: _dev(v) for k, v in w.items()}))
+        nbytes = gate_up_bytes("w4a16_g64", N, K, 2)
+        copies = max(2, -(-700_000_000 // nbytes))
+        x = _x_dev(wl.gen_x(K, 1, "f16", (9, c, 9)), "f16")
+        calls = []
+        for j in range(copies):
+            Ws = mats if j == 0 else [m.clone() for m in mats]
+            ys = [torch.empty((1, N), dtype=torch.float32, device="cuda") for _ in range(2)]
+            calls.append([(Ws[0], x, N, ys[0]), (Ws[1], x, N, ys[1])])
+
+        def run(calls=calls):
+            for items in calls:
+                qmv.matvec_grouped("w4a16_g64", items, K)
+        ms, _ = time_graph(run, 10, 3)
+        us = ms * 1e3 / copies
+        pts.append({"rows_per_matrix": N, "bytes": nbytes, "us": us, "gbs": nbytes / (us * 1e-6) / 1e9})
+        del calls, mats
+        torch.cuda.empty_cache()
+    b = np.array([p["bytes"] for p in pts], dtype=np.float64)
+    t = np.array([p["us"] for p in pts], dtype=np.float64)
+    slope, t0 = np.polyfit(b, t, 1)
+    return {"points": pts, "fit_t0_us": t0, "fit_steady_gbs": 1e-3 / slope,
+            "note": "t = t0 + bytes / steady_gbs, least squares over the four sizes"}
+
+
 def _sweep_result(ms, b, nbytes, launches, matvecs):
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"ms_per_token_step": ms, "tok_per_s": b / (ms * 1e-3), "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
@@ -403,6 +443,7 @@ LEGS = {
     "q8_0_512x512_b1_single": leg_q8_0,
     "q4k_0.6B_mlp_b1_cold": leg_mlp06,
     "q4k_vocab_head_151936x1024_b1_cold": leg_head06,
+    "stream_ramp_w4a16_gate_up_b1": leg_stream_ramp,
     "decode_sweep_1.1B_b1": lambda q: leg_sweep(q, 1),
     "decode_sweep_1.1B_b8": lambda q: leg_sweep(q, 8),
     "decode_sweep_1.1B_b1_fused": lambda q: leg_sweep_fused(q, 1),
