@@ -795,6 +795,10 @@ def gated_figures(out):
             g[tag] = {"gbs": r["gbs"], "frac_hbm": r["gbs"] / HBM_PEAK_GBS,
                       "tok_per_s" if "tok_per_s" in r else "tok_per_s_equiv":
                           r.get("tok_per_s", r.get("tok_per_s_equiv"))}
+    r = ex.get("stream_ramp_w4a16_gate_up_b1", {})
+    if "fit_steady_gbs" in r:
+        g["gate_up_launch_steady_state"] = {"fixed_us_per_launch": r["fit_t0_us"], "gbs": r["fit_steady_gbs"],
+                                            "frac_hbm": r["fit_steady_gbs"] / HBM_PEAK_GBS}
     r = ex.get("gemm_w4a16_M512", {})
     if "tflops" in r:
         g["c4_w4a16_gemm_M512"] = {"tflops": r["tflops"], "frac_bf16_mfma": r["frac_bf16_peak"],
