@@ -124,3 +124,78 @@ def test_epilogue_plain_equals_matvec_bitwise(qmv):
         c = qmv.matvec_ex(fmt, Wp, x, N, K)
         torch.cuda.synchronize()
         assert torch.equal(a.view(torch.int32), c.view(torch.int32)), (fmt, N, K, b)
+
+
+@pytest.mark.parametrize("batch", [1, 8])
+def test_fused_sweep_launch_configuration(qmv, batch):
+    # the timed fused decode token's own launches for one 1.1B layer plus the
+    # head: q + k + v grouped, o with the residual added in place, gate / up /
+    # SwiGLU in one launch writing h, down reading h with the residual added in
+    # place; every output against the oracle, the residual chain included
+    import bench
+    st = bench.FusedSweep(qmv, wl.c5_sweep(batch, layers=1), batch)
+    r0 = st.resid.cpu().numpy().astype(np.float64)
+    lay = st.layers[0]
+    xin = {k: lay[k].cpu().numpy().astype(np.float64) for k in ("attn_in", "o_in", "mlp_in")}
+    st()
+    torch.cuda.synchronize()
+    # one weight set per distinct shape (later matrices of that shape get
+    # copies of it), seeded with the key of the shape's first matrix
+    shapes = {nm: (fmt, N, K) for nm, fmt, N, K in wl.C5_LAYER}
+    first = {}
+    for i, (nm, fmt, N, K) in enumerate(wl.C5_LAYER):
+        first.setdefault((fmt, N, K), (5, 0, i))
+    keys = {nm: first[shapes[nm]] for nm in shapes}
+
+    def prod(nm, x):
+        fmt, N, K = shapes[nm]
+        W32 = oracle.dequant(fmt, wl.gen_weights(fmt, N, K, keys[nm]))
+        return oracle.matvec_ref(W32, x), oracle.tolerance_bound(W32, x, TAU)
+
+    for nm in ("q", "k", "v"):
+        y, b = prod(nm, xin["attn_in"])
+        r = oracle.check_within(lay[nm].cpu().numpy(), y, b)
+        _say("fused sweep", batch, nm, r)
+        assert r["ok"], (nm, r)
+    yo, bo = prod("o", xin["o_in"])
+    r1 = oracle.epilogue_ref(yo, None, r0)
+    b1 = oracle.epilogue_bound(bo, yo, None, r0)
+    g, dg = prod("gate", xin["mlp_in"])
+    u, du = prod("up", xin["mlp_in"])
+    h = lay["h"].cpu().numpy()
+    r = oracle.check_within(h, oracle.swiglu_ref(g, u), oracle.swiglu_bound(g, u, dg, du))
+    _say("fused sweep", batch, "swiglu", r)
+    assert r["ok"], r
+    # down reads the kernel's own h (its error is checked above); the residual
+    # it adds to carries the o step's bound
+    yd, bd = prod("down", h.astype(np.float64))
+    r2 = oracle.epilogue_ref(yd, None, r1)
+    b2 = oracle.epilogue_bound(bd, yd, None, r1) + b1
+    r = oracle.check_within(st.resid.cpu().numpy(), r2, b2)
+    _say("fused sweep", batch, "residual chain", r)
+    assert r["ok"], r
+    Wh, xh, yh, V = st.head
+    W32 = oracle.dequant("q6k", wl.gen_weights("q6k", V, 2048, (5, 1000, 7)))
+    xv = xh.cpu().numpy().astype(np.float64)
+    r = oracle.check_within(yh.cpu().numpy(), oracle.matvec_ref(W32, xv), oracle.tolerance_bound(W32, xv, TAU))
+    _say("fused sweep", batch, "head", r)
+    assert r["ok"], r
+
+
+@pytest.mark.parametrize("fmt,N,K", [("q6k", 2048, 5632), ("q4k", 2048, 2048), ("w4a16_g64", 2048, 5632),
+                                     ("q8_0", 1, 64), ("q4k", 17, 256), ("q5_0", 1, 32)])
+@pytest.mark.parametrize("batch", [1, 8])
+def test_residual_epilogue_sizes(qmv, fmt, N, K, batch):
+    # the decoder's o / down shapes with the residual added in place, and the
+    # smallest and ragged shapes (one row, 17 rows, one block of K)
+    xd = XDT.get(fmt, "f32")
+    w = wl.gen_weights(fmt, N, K, (66, N, K))
+    x = wl.gen_x(K, batch, xd, (66, N, K))
+    res = np.random.default_rng(N + K).normal(0, 2, (batch, N)).astype(np.float32)
+    rd = dev(res)
+    qmv.matvec_ex(fmt, pack_dev(qmv, fmt, w), dev_x(x, xd), N, K, y=rd, residual=rd)
+    torch.cuda.synchronize()
+    y, b = _prod(fmt, w, x, xd)
+    r = oracle.check_within(rd.cpu().numpy(), oracle.epilogue_ref(y, None, res), oracle.epilogue_bound(b, y, None, res))
+    _say("residual", fmt, N, K, batch, r)
+    assert r["ok"], r

@@ -164,3 +164,20 @@ def test_q8x_rejects_dense_bf16(qmv):
     x = wl.gen_x(K, 1, "f32", (77, 0, 0))
     with pytest.raises(qmv.QmvError, match="DENSE_BF16"):
         qmv.matvec("bf16", pack_dev(qmv, "bf16", w), qmv.quantize_x(dev(x)), N, K)
+
+
+@pytest.mark.parametrize("fmt,N,K", [("q4k", 5632, 2048), ("q6k", 2048, 5632), ("w4a16_g64", 5632, 2048),
+                                     ("q8_0", 1, 32), ("q5k", 17, 256), ("i8row", 3, 64)])
+@pytest.mark.parametrize("batch", [1, 8])
+def test_q8x_matvec_sizes(qmv, fmt, N, K, batch):
+    # the decoder's gate / down shapes (every row), and one row, 17 rows, one block of K
+    _say("q8x sizes", fmt, N, K, batch)
+    w = wl.gen_weights(fmt, N, K, (78, N, K))
+    x = wl.gen_x(K, batch, "f32", (78, N, K))
+    q, d, buf = _q8x_input(x)
+    y = qmv.matvec(fmt, pack_dev(qmv, fmt, w), qmv.Q8X(buf, K, batch), N, K)
+    torch.cuda.synchronize()
+    W32 = oracle.dequant(fmt, w)
+    xh = oracle.dequant_q8x(q, d)
+    r = oracle.check_within(y.cpu().numpy(), oracle.matvec_ref(W32, xh), oracle.tolerance_bound(W32, xh, TAU))
+    assert r["ok"], r
