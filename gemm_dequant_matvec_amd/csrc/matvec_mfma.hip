@@ -132,10 +132,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 
 // High or low bf16 part of two activations, packed.
-// The value of lane l ^ 16 (ds_swizzle, bit-mask mode: and 0x1F, xor 0x10).
-__device__ __forceinline__ float swap_rows(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
-}
 
 // The value of the adjacent lane (0 <-> 1, 2 <-> 3, ...): DPP quad_perm [1,0,3,2].
 __device__ __forceinline__ float swap_pair(float v) {
@@ -391,8 +387,11 @@ struct Staging {
         acc1 = fmaf(s, fmaf(-128.0f, dx[2] + dx[3], dq[2] + dq[3]), acc1);
       }
     } else {  // Q6K
-      const int sh_q = 4 * (G & 1);
-      const int sh_h = 4 * (G >> 1) + 2 * (G & 1);
+      // lane group G takes k = 4G .. 4G + 3 of each 16-k sub-block: bytes
+      // 2 (G % 2), + 1 of code word G / 2, both nibbles (k in order), with the
+      // high bits of that word's even / odd codes (qh bits 4 (G / 2) + 0 / 2)
+      const int g2 = G >> 1;
+      const uint32_t selp = (G & 1) ? 0x07030602u : 0x05010400u;  // (even, odd, even, odd) codes of 2 bytes
       const s16x4 ones4 = {0x3F80, 0x3F80, 0x3F80, 0x3F80};
       const float d = f16f(st.d);
       const u32x4 sv = *reinterpret_cast<const u32x4*>(lds + 768 + 4 * r);
@@ -402,8 +401,10 @@ struct Staging {
         const u32x2 hw = *reinterpret_cast<const u32x2*>(lds + 512 + 16 * r + 4 * ((f >> 1) ^ swz4(r)) + 2 * (f & 1));
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          const uint32_t qlw = lds[32 * r + 4 * (f ^ swz8(r)) + 2 * s + (G >> 1)];
-          const uint32_t v = ((qlw >> sh_q) & 0x0F0F0F0Fu) | (((hw[s] >> sh_h) & 0x03030303u) << 4);
+          const uint32_t qlw = lds[32 * r + 4 * (f ^ swz8(r)) + 2 * s + g2];
+          const uint32_t ev = (qlw & 0x0F0F0F0Fu) | (((hw[s] >> (4 * g2)) & 0x03030303u) << 4);
+          const uint32_t od = ((qlw >> 4) & 0x0F0F0F0Fu) | (((hw[s] >> (4 * g2 + 2)) & 0x03030303u) << 4);
+          const uint32_t v = __builtin_amdgcn_perm(od, ev, selp);
           const u32x2 bw = {code_pair<0x04010400u>(v), code_pair<0x04030402u>(v)};
           const u32x2 aa = {aw[2 * s], aw[2 * s + 1]};
           const s16x4 a4 = __builtin_bit_cast(s16x4, aa);
@@ -426,8 +427,9 @@ struct Staging {
 //   W4A16       k = 64(u/2) + 16G + 8(u%2) + e    (one 8-byte read per lane serves both halves
 //                                                  of the 64-k group)
 //   Q6K         two 16x16x16 MFMAs, sub-block s = 0, 1:
-//               k = 32u + 16s + 8(G/2) + 2e + G%2  (e = 0..3: one byte lane of one 6-bit code
-//                                                  word; elements 4s + e of the A fragment)
+//               k = 32u + 16s + 4G + e           (e = 0..3: two bytes of one code word, even
+//                                                  and odd codes interleaved by one permute;
+//                                                  elements 4s + e of the A fragment)
 //
 // One workgroup's share of one segment: stage is the workgroup's staging LDS
 // (SD dwords per wave), red its reduction LDS.
@@ -491,31 +493,21 @@ __device__ __forceinline__ void mfma_segment(const TB& tb, const MSeg& sg, uint3
     const int uc = min(u, U - 1);
     const bool ok = vec_ok && u < U;
     float v[8];
-    if constexpr (FMT == QMV_Q6K) {  // f32 x: k = 32u + 16s + 8(G/2) + (G%2) + 2e
-      const uint32_t odd = 0u - static_cast<uint32_t>(G & 1);
-      // the 8 consecutive values of a sub-block are needed by four lanes: the
-      // high / low pair (adjacent lanes) of both lane groups G and G ^ 1 (16
-      // lanes apart); each loads two and the rest arrive by a DPP pair swap and
-      // a ds_swizzle across the 16-lane rows
-      const int par = G & 1;
+    if constexpr (FMT == QMV_Q6K) {  // f32 x: k = 32u + 16s + 4G + e (the code words are interleaved to match)
+      // the two lanes of a high / low pair need the same 4 values of a
+      // sub-block: each loads two and takes the other two from its partner.
+      // No zeroing: a padding vector's A rows only reach D rows that are never
+      // stored, and a wave's chunks past K are never multiplied (K is a
+      // multiple of 256)
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        float t[8];
-        const f32x2 mine = *reinterpret_cast<const f32x2*>(static_cast<const float*>(a.x) + xrow + 32 * uc + 16 * s +
-                                                           8 * (G >> 1) + 4 * par + 2 * low);
-        const float m0 = ok ? mine[0] : 0.0f, m1 = ok ? mine[1] : 0.0f;
-        const float o0 = swap_pair(m0), o1 = swap_pair(m1);
-        const float h[4] = {low ? o0 : m0, low ? o1 : m1, low ? m0 : o0, low ? m1 : o1};  // values 4 par ..
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float g = swap_rows(h[i]);  // values 4 (par ^ 1) + i
-          t[i] = par ? g : h[i];
-          t[4 + i] = par ? h[i] : g;
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e)  // odd or even element by mask (a select would become a lane-varying index)
-          v[4 * s + e] = __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, t[2 * e + 1]) & odd) |
-                                                       (__builtin_bit_cast(uint32_t, t[2 * e]) & ~odd));
+        const f32x2 mine =
+            *reinterpret_cast<const f32x2*>(static_cast<const float*>(a.x) + xrow + 32 * uc + 16 * s + 4 * G + 2 * low);
+        const float o0 = swap_pair(mine[0]), o1 = swap_pair(mine[1]);
+        v[4 * s] = low ? o0 : mine[0];
+        v[4 * s + 1] = low ? o1 : mine[1];
+        v[4 * s + 2] = low ? mine[0] : o0;
+        v[4 * s + 3] = low ? mine[1] : o1;
       }
     } else if constexpr (!XF16) {
       // f32 x: the two lanes of a high / low pair (adjacent lanes) need the same
