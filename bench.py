@@ -95,8 +95,14 @@ def matvec_bytes(fmt, N, K, batch, x_bytes_per_el):
     return int(round(wl.bytes_per_weight(fmt) * N * K)) + batch * K * x_bytes_per_el + batch * N * 4
 
 
+REPLAY_STATS = {}  # per-replay statistics of the last time_graph call (median / min / p90 ms)
+
+
 def time_graph(fn, steps, warmup, stream=None):
-    """Capture fn() once into a HIP graph, replay warmup + steps times; ms per replay."""
+    """Capture fn() once into a HIP graph, replay warmup + steps times; ms per
+    replay over the timed replays (one event before and one after them).  Then
+    `steps` more replays with an event after each give the median, min and p90
+    of single replays (REPLAY_STATS; the markers are kept out of the timed pass)."""
     import torch
     s = stream or torch.cuda.Stream()
     fn()  # eager once (argument checks, lazy init)
@@ -116,7 +122,20 @@ def time_graph(fn, steps, warmup, stream=None):
         t1.record(s)
     t1.synchronize()
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / steps, g
+    ms = t0.elapsed_time(t1) / steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    with torch.cuda.stream(s):
+        ev[0].record(s)
+        for i in range(steps):
+            g.replay()
+            ev[i + 1].record(s)
+    ev[-1].synchronize()
+    torch.cuda.synchronize()
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    REPLAY_STATS.clear()
+    REPLAY_STATS.update({"replays": steps, "median_ms": per[len(per) // 2], "min_ms": per[0],
+                         "p90_ms": per[min(len(per) - 1, (9 * len(per)) // 10)]})
+    return ms, g
 
 
 class Stream:
@@ -217,6 +236,7 @@ def headline(qmv, args):
     import workloads as wl
     st = MlpStream(qmv, wl.c2_w4a16_mlp(), args.copies)
     ms, _ = time_graph(st, args.steps, args.warmup)
+    st.replay_stats = dict(REPLAY_STATS)
     gbs = st.bytes / (ms * 1e-3) / 1e9
     return st, ms, gbs
 
@@ -326,7 +346,7 @@ def platform_probes(qmv):
 
 
 def _gbs_result(d, gbs):
-    d.update({"gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+    d.update({"gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS, "replays": dict(REPLAY_STATS),
               "tok_per_s_equiv": gbs * 1e9 / TOKEN_BYTES_1B1,
               "tok_note": "GB/s / bytes of one 1.1B decode token (667152384 B)"})
     return d
@@ -347,7 +367,7 @@ def leg_mlp06(qmv):
     import workloads as wl
     mlp = [m for m in wl.c3_q4k_0b6()["mats"] if m[0] != "head"]
     st = Stream(qmv, mlp, "f32", 1, 170)
-    ms, _ = time_graph(st, 10, 3)
+    ms, _ = time_graph(st, 20, 3)
     return _gbs_result({"us_per_launch": ms * 1e3 / st.launches, "launches": st.launches},
                        st.bytes / (ms * 1e-3) / 1e9)
 
@@ -357,7 +377,7 @@ def leg_head06(qmv):
     import workloads as wl
     head = [m for m in wl.c3_q4k_0b6()["mats"] if m[0] == "head"]
     st = Stream(qmv, head, "f32", 1, 8)
-    ms, _ = time_graph(st, 10, 3)
+    ms, _ = time_graph(st, 20, 3)
     return _gbs_result({"us_per_launch": ms * 1e3 / st.launches, "bytes_per_launch": st.bytes // st.launches},
                        st.bytes / (ms * 1e-3) / 1e9)
 
@@ -405,14 +425,14 @@ def leg_stream_ramp(qmv):
 def _sweep_result(ms, b, nbytes, launches, matvecs):
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"ms_per_token_step": ms, "tok_per_s": b / (ms * 1e-3), "gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
-            "bytes": nbytes, "launches": launches, "matvecs": matvecs}
+            "bytes": nbytes, "launches": launches, "matvecs": matvecs, "replays": dict(REPLAY_STATS)}
 
 
 def leg_sweep(qmv, b):
     """One decode token of the 1.1B decoder at batch b: 155 matvecs, 667 MB of weights."""
     import workloads as wl
     st = Sweep(qmv, wl.c5_sweep(b), b)
-    ms, _ = time_graph(st, 10, 3)
+    ms, _ = time_graph(st, 20, 3)
     return _sweep_result(ms, b, st.bytes, st.launches, st.matvecs)
 
 
@@ -422,7 +442,7 @@ def leg_sweep_q8x(qmv, b):
     import workloads as wl
     st = Sweep(qmv, wl.c5_sweep(b), b)
     step = st.with_q8x()
-    ms, _ = time_graph(step, 10, 3)
+    ms, _ = time_graph(step, 20, 3)
     r = _sweep_result(ms, b, step.bytes, step.launches, st.matvecs)
     r["note"] = "bytes as the f32 sweep; launches include one quantize per distinct x"
     return r
@@ -433,7 +453,7 @@ def leg_sweep_fused(qmv, b):
     gate / up / SwiGLU in one pass (h written once)."""
     import workloads as wl
     st = FusedSweep(qmv, wl.c5_sweep(b), b)
-    ms, _ = time_graph(st, 10, 3)
+    ms, _ = time_graph(st, 20, 3)
     return _sweep_result(ms, b, st.bytes, st.launches, st.matvecs)
 
 
@@ -630,7 +650,8 @@ def gemm_leg(qmv, M, reps=20):
     def run():
         for _ in range(reps):
             qmv.gemm(fmt, W, X, N, K, Y=Y)
-    ms, _ = time_graph(run, 10, 3)
+    ms, _ = time_graph(run, 20, 3)
+    rs = dict(REPLAY_STATS)  # per replay of `reps` launches
     ms /= reps
     flops = 2.0 * M * N * K
     tf = flops / (ms * 1e-3) / 1e12
@@ -657,6 +678,7 @@ def gemm_leg(qmv, M, reps=20):
     del WdT
     return {"us": ms * 1e3, "tflops": tf, "frac_bf16_peak": tf / BF16_PEAK_TFLOPS,
             "tok_per_s": M / (ms * 1e-3), "prefill_tok_per_s_equiv": tf * 1e12 / TOKEN_FLOPS_1B1,
+            "replays_of_20_launches": rs,
             "matvec_path_us": ms_mv * 1e3, "dense_bf16_library_gemm_us": ms_bl * 1e3,
             "dense_bf16_library_frac_peak": flops / (ms_bl * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
 
@@ -847,7 +869,8 @@ def main():
         "config": {"workload": "W4A16-g64 decode matvec, 1.1B-decoder MLP (gate, up 5632x2048 "
                                "as one grouped launch; down 2048x5632), batch 1, fp16 x",
                    "copies": args.copies, "launches_per_step": st.launches,
-                   "bytes_per_step": st.bytes, "frac_of_peak": gbs / HBM_PEAK_GBS},
+                   "bytes_per_step": st.bytes, "frac_of_peak": gbs / HBM_PEAK_GBS,
+                   "replays": st.replay_stats},
         "roofline": roofline,
     }
     log("copy probe")
