@@ -484,8 +484,8 @@ __device__ __forceinline__ void mfma_segment(const TB& tb, const MSeg& sg, uint3
   };
   Stage<FMT> SA = vload(0, u0), SB;
 
-  // ---- A operands of this wave's K slice, built once (zero past K and for
-  // vectors >= nv, so those fragments and parts contribute nothing)
+  // ---- A operands of this wave's K slice, built once (the fp16 path zeroes
+  // them past K and for vectors >= nv; the f32 paths need not, see there)
   bf16x8 A[KF];
 #pragma unroll
   for (int f = 0; f < KF; ++f) {
@@ -512,12 +512,15 @@ __device__ __forceinline__ void mfma_segment(const TB& tb, const MSeg& sg, uint3
     } else if constexpr (!XF16) {
       // f32 x: the two lanes of a high / low pair (adjacent lanes) need the same
       // 8 values; each loads one half and takes the other from its partner,
-      // halving the activation traffic
+      // halving the activation traffic.  No zeroing, as for Q6K: padding
+      // vectors reach only D rows that are never stored, and fragments past K
+      // are never multiplied (Q4K: K is a multiple of 256; W4A16 / Q8_0: the
+      // compute loops stop at U)
       const int k0 = (FMT == QMV_W4A16_G64) ? 64 * (uc >> 1) + 16 * G + 8 * (uc & 1) : 32 * uc + 8 * G;
       const f32x4 mine = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.x) + xrow + k0 + 4 * low);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float m = ok ? mine[i] : 0.0f;
+        const float m = mine[i];
         const float o = swap_pair(m);
         v[i] = low ? o : m;
         v[4 + i] = low ? m : o;
