@@ -267,16 +267,16 @@ def matvec_ex(fmt, W: torch.Tensor, x: torch.Tensor, N: int, K: int, y: torch.Te
         raise ValueError("y dtype must be float32, float16 or bfloat16")
     _need(W, packed_bytes(fmt, N, K), "W")
     _need(y, b * N * 4, "y")
-    ep = QmvEpilogue()
     if bias is not None:
         _need_dtype(bias, torch.float32, "bias")
         _need(bias, N * 4, "bias")
-        ep.bias = _ptr(bias)
     if residual is not None:
         _need_dtype(residual, torch.float32, "residual")
         _need(residual, b * N * 4, "residual")
-        ep.residual = _ptr(residual)
-    xp, xdt, b, _ = _xarg(x, K)
+    xp, xdt, b, _ = _xarg(x, K)  # every size check above: pointers only from here on
+    ep = QmvEpilogue()
+    ep.bias = _ptr(bias)
+    ep.residual = _ptr(residual)
     _check(_lib.qmv_matvec_ex(_fmt(fmt), N, K, b, _ptr(W), xp, xdt, _ptr(y),
                               _DTYPES[y.dtype], ctypes.byref(ep), _stream(stream)))
     return y

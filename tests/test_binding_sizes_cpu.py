@@ -84,3 +84,41 @@ def test_pack_short_logical_arrays_and_out():
         qmv.pack("q4k", missing, N, K, out=_u8(need))
     with pytest.raises(ValueError, match="q holds"):  # two stacked matrices need twice the codes
         qmv.pack("q4k", lg, N, K, batch=2, out=_u8(2 * need))
+
+
+def test_epilogue_short_buffers():
+    N, K, b = 64, 256, 3
+    need = qmv.packed_bytes("q4k", N, K)
+    x = torch.zeros((b, K))
+    y = torch.zeros((b, N))
+    with pytest.raises(ValueError, match="bias holds"):
+        qmv.matvec_ex("q4k", _u8(need), x, N, K, y=y, bias=torch.zeros(N - 1), residual=torch.zeros((b, N)))
+    with pytest.raises(ValueError, match="residual holds"):
+        qmv.matvec_ex("q4k", _u8(need), x, N, K, y=y, bias=torch.zeros(N), residual=torch.zeros((b - 1, N)))
+    with pytest.raises(ValueError, match="bias must be"):
+        qmv.matvec_ex("q4k", _u8(need), x, N, K, y=y, bias=torch.zeros(N, dtype=torch.float16))
+    with pytest.raises(ValueError, match="GPU"):
+        qmv.matvec_ex("q4k", _u8(need), x, N, K, y=y, bias=torch.zeros(N), residual=torch.zeros((b, N)))
+    with pytest.raises(ValueError, match="W_up holds"):
+        qmv.matvec_swiglu("q4k", _u8(need), _u8(need - 1), x, N, K, h=y)
+    with pytest.raises(ValueError, match="h holds"):
+        qmv.matvec_swiglu("q4k", _u8(need), _u8(need), x, N, K, h=torch.zeros((b, N - 1)))
+
+
+def test_q8x_short_buffers():
+    K, b = 256, 2
+    nbytes = qmv.q8x_bytes(K, b)
+    assert nbytes == b * ((K + K // 8 + 15) // 16 * 16)
+    with pytest.raises(ValueError, match="out holds"):
+        qmv.quantize_x(torch.zeros((b, K)), out=_u8(nbytes - 1))
+    with pytest.raises(ValueError, match="x must be"):
+        qmv.quantize_x(torch.zeros((b, K), dtype=torch.float16), out=_u8(nbytes))
+    N = 32
+    need = qmv.packed_bytes("q6k", N, K)
+    with pytest.raises(ValueError, match="x holds"):
+        qmv.matvec("q6k", _u8(need), qmv.Q8X(_u8(nbytes - 16), K, b), N, K, y=torch.zeros((b, N)))
+    with pytest.raises(ValueError, match="K=512"):
+        qmv.matvec("q6k", _u8(qmv.packed_bytes("q6k", N, 512)), qmv.Q8X(_u8(nbytes), K, b), N, 512,
+                   y=torch.zeros((b, N)))
+    with pytest.raises(ValueError, match="GPU"):
+        qmv.matvec("q6k", _u8(need), qmv.Q8X(_u8(nbytes), K, b), N, K, y=torch.zeros((b, N)))
