@@ -561,6 +561,11 @@ hipError_t launch_matvec_epi(int fmt, int64_t N, int64_t K, int64_t batch, const
       if (e != hipSuccess) return e;
       continue;
     }
+    // a last chunk of one vector (batch 9, 17, ...) on the streaming kernel
+    if (nb == 1 && launch_matvec_b1_epi(fmt, N, K, W, W2, xb, x_dtype, yb, bias, ea.res, s, &e)) {
+      if (e != hipSuccess) return e;
+      continue;
+    }
     if (q8) {
       switch (fmt) {
         case QMV_Q8_0: e = pick_lpr<QMV_Q8_0, false, true>(W, p, xb, yb, int(N), int(K), nb, ea, s); break;

@@ -38,7 +38,7 @@ SHAPES = [(100, 256), (130, 512), (200, 1024), (129, 2048), (70, 5632)]
 
 
 @pytest.mark.parametrize("fmt", ["q4k", "q6k", "w4a16_g64", "q8_0", "q5k", "i8row"])
-@pytest.mark.parametrize("batch", [1, 3, 8])
+@pytest.mark.parametrize("batch", [1, 3, 8, 9])
 def test_bias_and_residual_epilogue(qmv, fmt, batch):
     for N, K in SHAPES:
         if K % wl.BLOCK[fmt]:
@@ -67,7 +67,7 @@ def test_bias_and_residual_epilogue(qmv, fmt, batch):
 
 
 @pytest.mark.parametrize("fmt", wl.FORMATS)
-@pytest.mark.parametrize("batch", [1, 2, 8, 11])
+@pytest.mark.parametrize("batch", [1, 2, 8, 9, 11])
 def test_swiglu(qmv, fmt, batch):
     for N, K in SHAPES:
         if K % wl.BLOCK[fmt]:

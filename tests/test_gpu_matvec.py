@@ -111,7 +111,7 @@ SHAPES = {  # (N, K) spanning lanes-per-row 16 / 32 / 64, ragged passes and ragg
 
 
 @pytest.mark.parametrize("fmt", wl.FORMATS)
-@pytest.mark.parametrize("batch", [1, 2, 3, 8, 11])
+@pytest.mark.parametrize("batch", [1, 2, 3, 8, 9, 11])
 def test_matvec_parity(qmv, fmt, batch):
     for N, K in SHAPES[fmt]:
         for xd in XDT[fmt]:
