@@ -13,14 +13,18 @@
 //     with its low 16 bits cleared (exact in bf16), low = the rest, rounded to
 //     bf16 (|error| <= 2^-16 |x|).  No padding rows at batch 8.
 //   * D (16 x 16, f32): per weight row and part, sum_k (128 + q) * part.
-//     high + low is added in f32, the 128 offset is removed with the block's
-//     sum of x (one MFMA of A against ones, done once per launch), and the
-//     block scale and min are applied in f32 in the same order as the
-//     dequantization formulas, so a one-hot x returns the dequantized column
-//     bit for bit.
+//     high + low is added in f32, the offset is removed with the block's
+//     sum of the parts (an MFMA of A against ones; Q6K, whose sub-blocks have
+//     no min, instead runs its code MFMA on top of an MFMA of A against -160,
+//     which leaves sum_k (q - 32) * part), and the block scale and min are
+//     applied in f32 in the same order as the dequantization formulas, so a
+//     one-hot x returns the dequantized column bit for bit.
+//   * Set-up: the two lanes of a high / low pair each load half of the
+//     pair's activations, split them into both parts and swap the part the
+//     other lane needs (one DPP move per two values).
 // Work layout: a workgroup of W waves owns one 16-row tile at a time and
 // strides over tiles; wave w owns KF consecutive blocks of K and keeps their
-// A operands and block sums in registers for the whole launch.  The W partial
+// A operands in registers for the whole launch.  The W partial
 // sums of a tile meet in LDS and are added in wave order (deterministic).
 //
 // Lane layout of v_mfma_f32_16x16x32_bf16 (and 16x16x16 with 4 elements):
@@ -144,6 +148,27 @@ __device__ __forceinline__ uint32_t part_pair(float a, float b, bool low) {
   return pack_bf16x2(low ? a - ha : ha, low ? b - hb : hb);
 }
 
+// Both bf16 parts of two activations a, b, packed: hi = the values with
+// their low 16 bits cleared (exact), lo = the rest rounded to bf16.
+__device__ __forceinline__ void parts2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  const uint32_t ab = __builtin_bit_cast(uint32_t, a), bb = __builtin_bit_cast(uint32_t, b);
+  hi = __builtin_amdgcn_perm(bb, ab, 0x07060302u);
+  lo = pack_bf16x2(a - __builtin_bit_cast(float, ab & 0xFFFF0000u), b - __builtin_bit_cast(float, bb & 0xFFFF0000u));
+}
+
+// A high / low lane pair (lanes 2i, 2i + 1: parts of one vector) each hold
+// two of four activations of one operand dword pair: the even lane the first
+// two (dword P0), the odd lane the last two (dword P1).  Each computes both
+// parts of its own two and sends its partner the part the partner needs, so
+// the pair's lanes end with (hi, hi) resp. (lo, lo) of all four in k order.
+__device__ __forceinline__ void exchange_parts(float a, float b, bool low, uint32_t& p0, uint32_t& p1) {
+  uint32_t hi, lo;
+  parts2(a, b, hi, lo);
+  const uint32_t got = __builtin_amdgcn_update_dpp(0, int(low ? hi : lo), 0xB1, 0xF, 0xF, false);
+  p0 = low ? got : hi;
+  p1 = low ? lo : got;
+}
+
 __device__ __forceinline__ bf16x8 as_bf8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   const u32x4 v = {a, b, c, d};
   return __builtin_bit_cast(bf16x8, v);
@@ -232,9 +257,8 @@ __device__ __forceinline__ int swz4(int r) { return (r >> 2) & 3; }
 __device__ __forceinline__ f32x4 mfma32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4 mfma16(const s16x4& a, const s16x4& b) {
-  const f32x4 z = {0, 0, 0, 0};
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, z, 0, 0, 0);
+__device__ __forceinline__ f32x4 mfma16(const s16x4& a, const s16x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ bf16x8 ones8() {
   bf16x8 o;
@@ -392,7 +416,7 @@ struct Staging {
       // high bits of that word's even / odd codes (qh bits 4 (G / 2) + 0 / 2)
       const int g2 = G >> 1;
       const uint32_t selp = (G & 1) ? 0x07030602u : 0x05010400u;  // (even, odd, even, odd) codes of 2 bytes
-      const s16x4 ones4 = {0x3F80, 0x3F80, 0x3F80, 0x3F80};
+      const s16x4 m160 = {-15584, -15584, -15584, -15584};  // bf16 -160 (0xC320)
       const float d = f16f(st.d);
       const u32x4 sv = *reinterpret_cast<const u32x4*>(lds + 768 + 4 * r);
 #pragma unroll
@@ -408,12 +432,13 @@ struct Staging {
           const u32x2 bw = {code_pair<0x04010400u>(v), code_pair<0x04030402u>(v)};
           const u32x2 aa = {aw[2 * s], aw[2 * s + 1]};
           const s16x4 a4 = __builtin_bit_cast(s16x4, aa);
-          const f32x4 dq = mfma16(a4, __builtin_bit_cast(s16x4, bw));
-          const f32x4 dx = mfma16(a4, ones4);
+          // sum_k part * (q - 32): the codes 128 + q against the parts, on top
+          // of -160 times the parts' sum (one MFMA of the parts against -160)
+          const f32x4 dq = mfma16(a4, __builtin_bit_cast(s16x4, bw), mfma16(a4, m160, z));
           const int j = 2 * f + s;  // sub-block within the super-block
           const float ds = d * static_cast<float>(static_cast<int8_t>((sv[j >> 2] >> (8 * (j & 3))) & 0xFFu));
-          acc0 = fmaf(ds, fmaf(-160.0f, dx[0] + dx[1], dq[0] + dq[1]), acc0);
-          acc1 = fmaf(ds, fmaf(-160.0f, dx[2] + dx[3], dq[2] + dq[3]), acc1);
+          acc0 = fmaf(ds, dq[0] + dq[1], acc0);
+          acc1 = fmaf(ds, dq[2] + dq[3], acc1);
         }
       }
     }
@@ -466,11 +491,10 @@ __device__ __forceinline__ void mfma_segment(const TB& tb, const MSeg& sg, uint3
   // ahead as soon as its chunk is in LDS, so the next tile's loads are in
   // flight while one tile is computed; the second set's first loads go out
   // after the set-up.  A set is never copied while its loads are in flight
-  // (the copy would wait for them).  With 16 fragments (two chunks per tile),
-  // and for Q6K, a second set does not fit in the registers next to the
-  // operands (the kernels spilled): one set is refilled with the following
-  // chunk.
-  constexpr bool TWO = KF == 8 && FMT != QMV_Q6K;
+  // (the copy would wait for them).  With 16 fragments (two chunks per tile)
+  // a second set does not fit in the registers next to the operands (the
+  // kernels spilled): one set is refilled with the following chunk.
+  constexpr bool TWO = KF == 8;
   // this workgroup's tiles bid, bid + nblk, ... (a segment has at most as many
   // workgroups as tiles); with SwiGLU each twice (virtual tiles n = 2i, 2i + 1)
   constexpr int VT = EPI == 2 ? 2 : 1;
@@ -492,45 +516,41 @@ __device__ __forceinline__ void mfma_segment(const TB& tb, const MSeg& sg, uint3
     const int u = u0 + f;
     const int uc = min(u, U - 1);
     const bool ok = vec_ok && u < U;
-    float v[8];
     if constexpr (FMT == QMV_Q6K) {  // f32 x: k = 32u + 16s + 4G + e (the code words are interleaved to match)
       // the two lanes of a high / low pair need the same 4 values of a
-      // sub-block: each loads two and takes the other two from its partner.
-      // No zeroing: a padding vector's A rows only reach D rows that are never
-      // stored, and a wave's chunks past K are never multiplied (K is a
-      // multiple of 256)
+      // sub-block (dwords 2s, 2s + 1): each loads two and exchanges parts
+      // with its partner.  No zeroing: a padding vector's A rows only reach D
+      // rows that are never stored, and a wave's chunks past K are never
+      // multiplied (K is a multiple of 256)
+      uint32_t p[4];
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const f32x2 mine =
             *reinterpret_cast<const f32x2*>(static_cast<const float*>(a.x) + xrow + 32 * uc + 16 * s + 4 * G + 2 * low);
-        const float o0 = swap_pair(mine[0]), o1 = swap_pair(mine[1]);
-        v[4 * s] = low ? o0 : mine[0];
-        v[4 * s + 1] = low ? o1 : mine[1];
-        v[4 * s + 2] = low ? mine[0] : o0;
-        v[4 * s + 3] = low ? mine[1] : o1;
+        exchange_parts(mine[0], mine[1], low, p[2 * s], p[2 * s + 1]);
       }
+      A[f] = as_bf8(p[0], p[1], p[2], p[3]);
     } else if constexpr (!XF16) {
       // f32 x: the two lanes of a high / low pair (adjacent lanes) need the same
-      // 8 values; each loads one half and takes the other from its partner,
+      // 8 values (dwords 0, 1 from the even lane's load, 2, 3 from the odd
+      // lane's); each loads one half and exchanges parts with its partner,
       // halving the activation traffic.  No zeroing, as for Q6K: padding
       // vectors reach only D rows that are never stored, and fragments past K
       // are never multiplied (Q4K: K is a multiple of 256; W4A16 / Q8_0: the
       // compute loops stop at U)
       const int k0 = (FMT == QMV_W4A16_G64) ? 64 * (uc >> 1) + 16 * G + 8 * (uc & 1) : 32 * uc + 8 * G;
       const f32x4 mine = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.x) + xrow + k0 + 4 * low);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float m = mine[i];
-        const float o = swap_pair(m);
-        v[i] = low ? o : m;
-        v[4 + i] = low ? m : o;
-      }
+      uint32_t p[4];
+      exchange_parts(mine[0], mine[1], low, p[0], p[2]);
+      exchange_parts(mine[2], mine[3], low, p[1], p[3]);
+      A[f] = as_bf8(p[0], p[1], p[2], p[3]);
     } else {
       const int k0 = (FMT == QMV_W4A16_G64) ? 64 * (uc >> 1) + 16 * G + 8 * (uc & 1) : 32 * uc + 8 * G;
+      float v[8];
       load_x8<XF16>(a.x, xrow + k0, ok, v);
+      A[f] = as_bf8(part_pair(v[0], v[1], low), part_pair(v[2], v[3], low), part_pair(v[4], v[5], low),
+                    part_pair(v[6], v[7], low));
     }
-    A[f] = as_bf8(part_pair(v[0], v[1], low), part_pair(v[2], v[3], low), part_pair(v[4], v[5], low),
-                  part_pair(v[6], v[7], low));
     if ((f & 7) == 7) __builtin_amdgcn_sched_barrier(0);  // at most 8 fragments' raw activations live
   }
 
