@@ -593,6 +593,25 @@ __device__ __forceinline__ void mfma_segment(const TB& tb, const MSeg& sg, uint3
     }
     buf ^= 1;
   };
+  if constexpr (KF == 16) {
+    // a wave with two chunks and a single tile (a short, deep matrix: few
+    // tiles, one per workgroup) loads both chunks at once, the second into a
+    // second register set; otherwise one set is refilled as below
+    const int nch = (min(KF, U - u0) + 7) >> 3;  // chunks of this wave (1 or 2)
+    if (nch == 2 && ntl == 1) {
+      SB = vload(0, u0 + 8);
+      acc0 = acc1 = 0.0f;
+      stg.store(SA, lds);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      stg.compute(SA, lds, A, u0, acc0, acc1);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // operand reads done before the next store
+      stg.store(SB, lds);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      stg.compute(SB, lds, A + 8, u0 + 8, acc0, acc1);
+      finish(0);
+      return;
+    }
+  }
   if constexpr (!TWO) {
     const int nch = (min(KF, U - u0) + 7) >> 3;  // chunks of this wave (1 or 2)
     for (int n = 0;; ++n) {
