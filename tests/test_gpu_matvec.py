@@ -152,6 +152,26 @@ def test_batched_matvec_k_ranges(qmv, fmt, kcase, batch):
         assert r["ok"], (fmt, K, batch, xd, r)
 
 
+# More tiles than workgroups at K > 2048 (16 blocks of K per wave): workgroups
+# take one or two tiles in turn, with one weight register set refilled across
+# tiles, and the last wave of each tile holds one chunk (K = 2304: 72 blocks
+# over 5 waves).  The matrix-core launch caps the grid at 256 workgroups (512
+# for Q6K), so 263 / 513 tiles give some workgroups a second tile.
+@pytest.mark.parametrize("fmt,N", [("q4k", 4200), ("q6k", 8208), ("q8_0", 4200), ("w4a16_g64", 4200)])
+@pytest.mark.parametrize("batch", [3, 8])
+def test_batched_more_tiles_than_workgroups(qmv, fmt, N, batch):
+    K = 2304
+    w = wl.gen_weights(fmt, N, K, (23, N, batch))
+    for xd in XDT[fmt]:
+        print("tiles", fmt, N, K, batch, xd, flush=True)
+        x = wl.gen_x(K, batch, xd, (23, N, batch))
+        Wp = pack_dev(qmv, fmt, w)
+        y = qmv.matvec(fmt, Wp, dev_x(x, xd), N, K)
+        torch.cuda.synchronize()
+        r = check_every_row(fmt, w, y.cpu().numpy(), x_values(x, xd))
+        assert r["ok"], (fmt, N, K, batch, xd, r)
+
+
 # K cases of the single-vector kernel: one 32-weight unit per lane, K split
 # over 2 waves with a ragged second slice, over 2 and 3 waves in full, the
 # largest K with activations held in registers (4 waves for fp16 W4A16), and a
