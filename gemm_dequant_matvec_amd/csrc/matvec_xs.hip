@@ -358,8 +358,10 @@ __device__ __forceinline__ float unit_dot(const Raw<FMT>& w, const XUnit<FMT == 
     }
     return acc + (t0 + t1);
   } else {
-    // 4- and 6-bit codes b as t = 0.5 + b / 256 (b in mantissa bits 16..21 of
-    // 0.5, placed by one v_perm_b32): sum b x = 256 (sum t x - sum x / 2)
+    // 4- and 6-bit codes b as fp16 pairs (1024 + b_a, 1024 + b_b) (exact: one
+    // v_perm_b32 puts two code bytes under 0x64 high bytes), each half taken by
+    // a mixed-precision FMA (v_fma_mix_f32) against f32 x: sum b x = sum t x -
+    // 1024 sum x
     float ta = 0.0f, tb = 0.0f;
     const uint32_t wd[4] = {w.q.x, w.q.y, w.q.z, w.q.w};
 #pragma unroll
@@ -378,15 +380,21 @@ __device__ __forceinline__ float unit_dot(const Raw<FMT>& w, const XUnit<FMT == 
       }
       float t = (FMT == QMV_Q6K && i >= 2) ? tb : ta;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t sel = 0x07000C0Cu | (uint32_t(c) << 16);
-        t = fmaf(__builtin_bit_cast(float, __builtin_amdgcn_perm(0x3F000000u, ev, sel)), xu.v[8 * i + 2 * c], t);
-        t = fmaf(__builtin_bit_cast(float, __builtin_amdgcn_perm(0x3F000000u, od, sel)), xu.v[8 * i + 2 * c + 1], t);
+      for (int c = 0; c < 2; ++c) {
+        // bytes 2c, 2c + 1 of ev (k = 8i + 4c, + 2) and of od (k = 8i + 4c + 1, + 3)
+        constexpr uint32_t k64 = 0x64646464u;
+        const uint32_t sel = c ? 0x04030402u : 0x04010400u;
+        const half2_t he = as_h2(__builtin_amdgcn_perm(k64, ev, sel));
+        const half2_t ho = as_h2(__builtin_amdgcn_perm(k64, od, sel));
+        t = fmaf(static_cast<float>(he[0]), xu.v[8 * i + 4 * c], t);
+        t = fmaf(static_cast<float>(ho[0]), xu.v[8 * i + 4 * c + 1], t);
+        t = fmaf(static_cast<float>(he[1]), xu.v[8 * i + 4 * c + 2], t);
+        t = fmaf(static_cast<float>(ho[1]), xu.v[8 * i + 4 * c + 3], t);
       }
       if (FMT == QMV_Q6K && i >= 2) tb = t; else ta = t;
     }
-    const float qa = 256.0f * fmaf(-0.5f, xu.s0, ta);  // sum b x (Q6K: k < 16)
-    const float qb = 256.0f * fmaf(-0.5f, xu.s1, tb);  // Q6K: k >= 16
+    const float qa = fmaf(-1024.0f, xu.s0, ta);  // sum b x (Q6K: k < 16)
+    const float qb = fmaf(-1024.0f, xu.s1, tb);  // Q6K: k >= 16
     if constexpr (FMT == QMV_W4A16_G64) {
       const float s = f16_bits_to_f32(w.sz & 0xFFFFu), z = f16_bits_to_f32(w.sz >> 16);
       return fmaf(s, fmaf(-z, xu.s0, qa), acc);
