@@ -330,18 +330,22 @@ __device__ __forceinline__ float unit_dot(const Raw<FMT>& w, const XUnit<FMT == 
     const float zo = 1024.0f + f16_bits_to_f32(w.sz >> 16);  // exact
     return fmaf(s, fmaf(-zo, xu.s, dot), acc);
   } else if constexpr (FMT == QMV_Q8_0 || FMT == QMV_I8_ROW) {
-    // code u = q + 128 as t = 0.5 + u / 65536 (u in mantissa bits 8..15 of 0.5)
+    // codes u = q + 128 as exact fp16 pairs (1024 + u_a, 1024 + u_b), one byte
+    // permute per two, each half taken by a mixed-precision FMA against f32 x
     float tx = 0.0f;
     const uint32_t wd[8] = {w.q0.x, w.q0.y, w.q0.z, w.q0.w, w.q1.x, w.q1.y, w.q1.z, w.q1.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint32_t u = wd[i] ^ 0x80808080u;
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        tx = fmaf(__builtin_bit_cast(float, __builtin_amdgcn_perm(0x3F000000u, u, 0x070C000Cu | (c << 8))),
-                  xu.v[4 * i + c], tx);
+      constexpr uint32_t k64 = 0x64646464u;
+      const half2_t lo = as_h2(__builtin_amdgcn_perm(k64, u, 0x04010400u));
+      const half2_t hi = as_h2(__builtin_amdgcn_perm(k64, u, 0x04030402u));
+      tx = fmaf(static_cast<float>(lo[0]), xu.v[4 * i], tx);
+      tx = fmaf(static_cast<float>(lo[1]), xu.v[4 * i + 1], tx);
+      tx = fmaf(static_cast<float>(hi[0]), xu.v[4 * i + 2], tx);
+      tx = fmaf(static_cast<float>(hi[1]), xu.v[4 * i + 3], tx);
     }
-    const float ux = 65536.0f * fmaf(-0.5f, xu.s0, tx);  // sum (q + 128) x
+    const float ux = fmaf(-1024.0f, xu.s0, tx);  // sum (q + 128) x
     const float sc = FMT == QMV_Q8_0 ? f16_bits_to_f32(w.sc) : __builtin_bit_cast(float, w.sc);
     return fmaf(sc, fmaf(-128.0f, xu.s0, ux), acc);
   } else if constexpr (FMT == QMV_DENSE_BF16) {
