@@ -268,6 +268,22 @@ def test_one_hot_returns_dequantized_column_bit_exact(qmv, fmt):
             assert np.array_equal(y[i], W32[:, k]), (fmt, xd, k)
 
 
+@pytest.mark.parametrize("fmt", ["q4k", "q6k", "w4a16_g64", "q5k", "q8_0", "i8row"])
+@pytest.mark.parametrize("batch", [1, 8])
+def test_positive_near_constant_activations(qmv, fmt, batch):
+    # all-positive, nearly equal activations (1 + 0.01 N(0,1), and the same times
+    # 1000): the decode offsets (codes biased by 1024 or 128 and removed with
+    # the sum of x) cancel the most here, at the decoder's longest K
+    N, K = 300, 5632
+    w = wl.gen_weights(fmt, N, K, (24, N, K))
+    rng = np.random.default_rng(24 + batch)
+    for scale in (1.0, 1000.0):
+        x = (scale * (1.0 + 0.01 * rng.standard_normal((batch, K)))).astype(np.float32)
+        r, _, _ = check_matvec(qmv, fmt, w, x, "f32")
+        print("near-constant x", fmt, batch, scale, r["max_ratio"], flush=True)
+        assert r["ok"], (fmt, batch, scale, r)
+
+
 def test_q8_0_minus_128(qmv):
     N, K = 8, 64
     w = wl.gen_weights("q8_0", N, K, (17, 0, 0))
