@@ -374,17 +374,25 @@ struct Staging {
       const float d = f16f(m[0]), dmin = f16f(m[0] >> 16);
       const uint64_t lo = uint64_t(m[1]) | (uint64_t(m[2]) << 32);
       const uint64_t hi = uint64_t(m[2] >> 16) | (uint64_t(m[3]) << 16);
+      // per super-block: sum_j sc_j (sum q x)_j and sum_j m_j (sum x)_j, then
+      // d and dmin once (sc_j q and d sc_j q are exact for f16 d, so a one-hot
+      // x still returns (d sc_j) q - dmin m_j bit for bit)
+      float q0 = 0.0f, q1 = 0.0f, m0 = 0.0f, m1 = 0.0f;
 #pragma unroll
       for (int f = 0; f < 8; ++f) {
         const uint32_t w = lds[32 * r + 4 * (f ^ swz8(r)) + G];
         const f32x4 dq = mfma32(A[f], nib8(w), z);
         const f32x4 dx = mfma32(A[f], ones, z);
-        const float ds = d * static_cast<float>(static_cast<uint32_t>(lo >> (6 * f)) & 63u);
-        const float dm = dmin * static_cast<float>(static_cast<uint32_t>(hi >> (6 * f)) & 63u);
+        const float sc = static_cast<float>(static_cast<uint32_t>(lo >> (6 * f)) & 63u);
+        const float mj = static_cast<float>(static_cast<uint32_t>(hi >> (6 * f)) & 63u);
         const float s0 = dx[0] + dx[1], s1 = dx[2] + dx[3];
-        acc0 = fmaf(-dm, s0, fmaf(ds, fmaf(-128.0f, s0, dq[0] + dq[1]), acc0));
-        acc1 = fmaf(-dm, s1, fmaf(ds, fmaf(-128.0f, s1, dq[2] + dq[3]), acc1));
+        q0 = fmaf(sc, fmaf(-128.0f, s0, dq[0] + dq[1]), q0);
+        q1 = fmaf(sc, fmaf(-128.0f, s1, dq[2] + dq[3]), q1);
+        m0 = fmaf(mj, s0, m0);
+        m1 = fmaf(mj, s1, m1);
       }
+      acc0 = fmaf(-dmin, m0, fmaf(d, q0, acc0));
+      acc1 = fmaf(-dmin, m1, fmaf(d, q1, acc1));
     } else if constexpr (FMT == QMV_W4A16_G64) {
       const u32x4 sz = *reinterpret_cast<const u32x4*>(lds + 512 + 4 * r);
 #pragma unroll
