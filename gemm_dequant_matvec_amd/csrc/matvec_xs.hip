@@ -258,7 +258,8 @@ __device__ __forceinline__ XRaw16 fetch_x16(const void* xv, int64_t off) {
 }
 
 // fp16 x: from the fetched words `raw`; f32 x: from the block's LDS copy `xv`
-// at float offset `off`.  valid = false gives a zero slice.
+// at float offset `off` (a unit's 16-byte words XOR-permuted by the unit
+// index, as the staging stores them).  valid = false gives a zero slice.
 template <int FMT, bool XF16>
 __device__ __forceinline__ void load_x(XUnit<FMT == QMV_W4A16_G64 && XF16>& xu, const void* xv, int64_t off,
                                        bool valid, const XRaw16* raw) {
@@ -290,10 +291,11 @@ __device__ __forceinline__ void load_x(XUnit<FMT == QMV_W4A16_G64 && XF16>& xu, 
       }
     }
   } else {
+    const int u = int(off >> 5);
     const float4* xp = reinterpret_cast<const float4*>(static_cast<const float*>(xv) + off);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      float4 xx = valid ? xp[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      float4 xx = valid ? xp[i ^ (u & 7)] : make_float4(0.f, 0.f, 0.f, 0.f);
       xu.v[4 * i] = xx.x; xu.v[4 * i + 1] = xx.y; xu.v[4 * i + 2] = xx.z; xu.v[4 * i + 3] = xx.w;
     }
   }
@@ -629,9 +631,14 @@ __device__ __forceinline__ void xs_segment(const Seg& sg, const int K, const Epi
   XUnit<H2> xs[UPL];
   if constexpr (STAGE) {
     __shared__ uint4 xl[NXI * BT];  // XW rounded up to whole staging rounds
+    // f32: word c of unit u (8 words) at 8u + (c ^ (u % 8)), so the lanes of a
+    // row, which read different units' word c at once, hit different banks
+    // (linear, the 16 lanes 128 bytes apart all fell on the same 4 banks)
 #pragma unroll
-    for (int i = 0; i < NXI; ++i)  // unconditional: no load sinks into a branch
-      xl[int(threadIdx.x) + i * BT] = make_uint4(xst[4 * i], xst[4 * i + 1], xst[4 * i + 2], xst[4 * i + 3]);
+    for (int i = 0; i < NXI; ++i) {  // unconditional: no load sinks into a branch
+      const int w = int(threadIdx.x) + i * BT;
+      xl[XF16 ? w : w ^ ((w >> 3) & 7)] = make_uint4(xst[4 * i], xst[4 * i + 1], xst[4 * i + 2], xst[4 * i + 3]);
+    }
     lds_barrier();
     if constexpr (XF16) {
 #pragma unroll
