@@ -631,22 +631,25 @@ __device__ __forceinline__ void xs_segment(const Seg& sg, const int K, const Epi
   XUnit<H2> xs[UPL];
   if constexpr (STAGE) {
     __shared__ uint4 xl[NXI * BT];  // XW rounded up to whole staging rounds
-    // f32: word c of unit u (8 words) at 8u + (c ^ (u % 8)), so the lanes of a
-    // row, which read different units' word c at once, hit different banks
-    // (linear, the 16 lanes 128 bytes apart all fell on the same 4 banks)
+    // 16-byte word w at w ^ ((w / 8) % 8) (within its 128-byte row): the lanes
+    // of a row, which read the same word of different units at once, hit
+    // different banks (f32: word c of unit u at 8u + (c ^ (u % 8)); linear, the
+    // 16 lanes 128 bytes apart all fell on the same 4 banks)
 #pragma unroll
     for (int i = 0; i < NXI; ++i) {  // unconditional: no load sinks into a branch
       const int w = int(threadIdx.x) + i * BT;
-      xl[XF16 ? w : w ^ ((w >> 3) & 7)] = make_uint4(xst[4 * i], xst[4 * i + 1], xst[4 * i + 2], xst[4 * i + 3]);
+      xl[w ^ ((w >> 3) & 7)] = make_uint4(xst[4 * i], xst[4 * i + 1], xst[4 * i + 2], xst[4 * i + 3]);
     }
     lds_barrier();
     if constexpr (XF16) {
 #pragma unroll
       for (int j = 0; j < UPL; ++j) {
-        const uint4* xp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(xl) + 32 * uu[j]);
         XRaw16 w;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w.v[i] = xp[i];
+        for (int i = 0; i < 4; ++i) {
+          const int wi = 4 * uu[j] + i;  // fp16: 4 words per unit
+          w.v[i] = xl[wi ^ ((wi >> 3) & 7)];
+        }
         load_x<FMT, XF16>(xs[j], nullptr, 0, uv[j], &w);
       }
     } else {
