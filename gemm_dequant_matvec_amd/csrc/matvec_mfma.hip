@@ -709,8 +709,9 @@ int blocks_override() {
 // with the next tile's weights in flight, do less work in all (measured on
 // MI355X, one 1.1B decode step at batch 8: 128 / 192 / 256 / 384 / 512
 // workgroups: 0.937 / 0.831 / 0.794 / 0.832 / 0.828 ms; the grouped Q4K
-// gate+up 11.0 -> 8.6 us).  Q6K keeps one register set, so its tiles run back
-// to back: the 32000 x 2048 head took 22.1 us at 512 and 25.8 at 256.
+// gate+up 11.0 -> 8.6 us).  Q6K launches take 512: with one register set its
+// tiles ran back to back and the 32000 x 2048 head took 22.1 us at 512 and 25.8
+// at 256; with two sets the 1.1B step is the same at 256 and 512 (0.692 ms).
 template <int FMT, bool XF16, int KF>
 hipError_t go(MTable& t, hipStream_t s, const MEpi* ep = nullptr) {
   int64_t tiles[kMaxSeg], total = 0;
