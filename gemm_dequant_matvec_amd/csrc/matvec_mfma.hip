@@ -135,13 +135,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// High or low bf16 part of two activations, packed.
-
-// The value of the adjacent lane (0 <-> 1, 2 <-> 3, ...): DPP quad_perm [1,0,3,2].
-__device__ __forceinline__ float swap_pair(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
-}
-
+// High (low = false) or low bf16 part of two activations, packed.
 __device__ __forceinline__ uint32_t part_pair(float a, float b, bool low) {
   const float ha = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, a) & 0xFFFF0000u);
   const float hb = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, b) & 0xFFFF0000u);
@@ -164,6 +158,7 @@ __device__ __forceinline__ void parts2(float a, float b, uint32_t& hi, uint32_t&
 __device__ __forceinline__ void exchange_parts(float a, float b, bool low, uint32_t& p0, uint32_t& p1) {
   uint32_t hi, lo;
   parts2(a, b, hi, lo);
+  // the adjacent lane's value (0 <-> 1, 2 <-> 3, ...): DPP quad_perm [1,0,3,2]
   const uint32_t got = __builtin_amdgcn_update_dpp(0, int(low ? hi : lo), 0xB1, 0xF, 0xF, false);
   p0 = low ? got : hi;
   p1 = low ? lo : got;
@@ -500,8 +495,9 @@ __device__ __forceinline__ void mfma_segment(const TB& tb, const MSeg& sg, uint3
   // flight while one tile is computed; the second set's first loads go out
   // after the set-up.  A set is never copied while its loads are in flight
   // (the copy would wait for them).  With 16 fragments (two chunks per tile)
-  // a second set does not fit in the registers next to the operands (the
-  // kernels spilled): one set is refilled with the following chunk.
+  // a second set refilled across tiles does not fit in the registers next to
+  // the operands (the kernels spilled): one set is refilled with the following
+  // chunk, except on a wave with a single tile (below).
   constexpr bool TWO = KF == 8;
   // this workgroup's tiles bid, bid + nblk, ... (a segment has at most as many
   // workgroups as tiles); with SwiGLU each twice (virtual tiles n = 2i, 2i + 1)
