@@ -700,8 +700,8 @@ int blocks_override() {
 // Workgroups: up to 256 per launch, one per CU, or 512 for Q6K (tuning
 // override above), split over the segments in proportion to their tiles, at
 // least one and at most one per tile.  Every wave builds its activation
-// operands once per launch (about 500 vector instructions per wave for Q4K,
-// against about 230 per tile), so fewer workgroups that each take more tiles,
+// operands once per launch (about 340 vector instructions per wave for Q4K,
+// against about 165 per tile), so fewer workgroups that each take more tiles,
 // with the next tile's weights in flight, do less work in all (measured on
 // MI355X, one 1.1B decode step at batch 8: 128 / 192 / 256 / 384 / 512
 // workgroups: 0.937 / 0.831 / 0.794 / 0.832 / 0.828 ms; the grouped Q4K
