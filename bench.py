@@ -51,6 +51,24 @@ TOKEN_FLOPS_1B1 = 2 * 1_034_420_224
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published
 
+# The source pages' own figures, each with the hardware it was measured on:
+# context for the report, not targets and not comparable one to one (other
+# machines, whole-model runs with attention and sampling included).
+PAGES_CONTEXT = [
+    {"figure": "CPU decode, TinyLlama-1.1B / Llama-3.2-1B, Q4_K_M weights, 8-bit activations, batch 1",
+     "value": "128 / 113 tok/s", "hardware": "Apple M1 Pro, 8 threads (NEON dot product)",
+     "source": "aot-llm README, benchmark figures"},
+    {"figure": "Metal decode, same models, f32 activations, weights dequantized on the fly",
+     "value": "106 / 92 tok/s", "hardware": "Apple M1 Pro GPU", "source": "aot-llm README, Metal backend notes"},
+    {"figure": "Metal quantized matvec bandwidth, 1B-class decode", "value": "75-107 GB/s",
+     "hardware": "Apple M1 Pro GPU", "source": "aot-llm README, Metal backend notes"},
+    {"figure": "Metal prompt evaluation (batched, the prefill analogue), ~300-token prompts",
+     "value": "550-750 tok/s", "hardware": "Apple M1 Pro GPU", "source": "aot-llm README, benchmark figures"},
+    {"figure": "Qwen3-0.6B decode time per token: f32 / bf16 / per-row int8 weights",
+     "value": "231-234 / 252-254 / 119 ms", "hardware": "Apple M-series laptop, Metal (STREAM ~228 GB/s)",
+     "source": "zynfer PR 100, stages M2, M4 and M5"},
+]
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -879,6 +897,7 @@ def main():
         log("extras")
         out["extras"] = extras(qmv, args)
         out["gated"] = gated_figures(out)
+    out["pages_context"] = PAGES_CONTEXT
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(args)

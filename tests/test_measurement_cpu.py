@@ -106,3 +106,12 @@ def test_bench_token_constants_and_gated_figures():
     assert g["c5_decode_token_b1"] == {"gbs": 1600.0, "frac_hbm": 0.2, "tok_per_s": 2400.0}
     assert g["c3_q4k_vocab_head"]["tok_per_s_equiv"] == 6000.0
     assert "c4_w4a16_gemm_M512" not in g  # a leg that failed is left out, not faked
+
+
+def test_pages_context_names_hardware_and_source():
+    import bench
+    assert bench.PAGES_CONTEXT
+    for e in bench.PAGES_CONTEXT:
+        assert e["hardware"] and e["source"] and e["value"] and e["figure"]
+        assert "MI355X" not in e["hardware"]  # the pages measured other machines
+
